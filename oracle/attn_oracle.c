@@ -1,0 +1,336 @@
+/*
+ * attn_oracle.c -- CPU fp64 oracle for paged grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+ * GPU library is checked against.  Only the test suite, the smoke check and
+ * the CPU-baseline leg of the benchmark may load it.  It shares no code,
+ * header, table or constant with the GPU library (paged_kv_cache_20_amd/),
+ * and the library never calls it.
+ *
+ * What it computes (the pages print no attention arithmetic, so the core is
+ * the textbook definition of scaled dot-product attention written out):
+ *
+ *   for query row r of sequence s and query head h:
+ *     kh    = h / (n_head / n_head_kv)           contiguous GQA groups
+ *     last  = ctx_len[s] - R + r                 last key position it sees
+ *     score_t = (q . k_t) / sqrt(head_dim)       t = 0 .. last
+ *     out     = sum_t exp(score_t - max) v_t / sum_t exp(score_t - max)
+ *
+ * Problem statement taken from the pages:
+ *  - "kern manifest v7" schema, $defs.Batch: a call carries `rows` rows per
+ *    sequence -- 1 for a decode step, exactly 8 for a speculative round, or
+ *    the chunk's row count for a prefill chunk (one sequence).
+ *  - same schema, $defs.Fill "seq_len": a sequence's length counts the rows
+ *    already in the state plus this call's, so the call's own rows are the
+ *    last R positions of the context and row r sits at ctx_len - R + r.
+ *  - same schema, $defs.Domain: a paged KV block table indexes pages of
+ *    `stride` (16) token slots; token t of a sequence lives in page
+ *    table[t / P] at offset t % P.
+ *  - "Radiance Architecture Plugins -- declaring a model", section
+ *    "Declare: the metadata": head_dim is an input, never derived from the
+ *    hidden size and head count.
+ *  - same page, section "Declare: buffers and KV groups": the full KV group
+ *    is a paged, per-token, growing cache.
+ *
+ * Storage decoding is exact: a bf16 value is the top half of an IEEE single;
+ * an fp8 code is decoded from the OCP E4M3 ("E4M3FN") definition -- 1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 is
+ * NaN, exponent 0 is subnormal m * 2^-9 -- and multiplied by its page's fp32
+ * scale in double precision (4 significant bits times 24 is exact).
+ *
+ * fp8 quantisation (the append oracle) follows the reading stated with
+ * oracle_kv_append below.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_KV_BF16 = 0, ORC_KV_FP8 = 1 };
+
+static double orc_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP E4M3 value of a code, from the format definition. */
+double oracle_e4m3_value(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                 /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);         /* normal: (1 + m/8) 2^(e-7) */
+    return sign ? -v : v;
+}
+
+typedef struct {
+    const void *k_pool, *v_pool;
+    const float *k_scale, *v_scale;
+    int64_t n_pages;
+    const int32_t *block_table;
+    int max_pages, n_head_kv, d, P, kv_dtype;
+} orc_pool;
+
+/* One stored K or V element of token slot (page, kh, off), as a double. */
+static double orc_elem(const orc_pool *pl, int is_v, int64_t page, int kh, int off, int i)
+{
+    int64_t idx = ((page * pl->n_head_kv + kh) * (int64_t)pl->P + off) * pl->d + i;
+    if (pl->kv_dtype == ORC_KV_BF16) {
+        const uint16_t *p = (const uint16_t *)(is_v ? pl->v_pool : pl->k_pool);
+        return orc_bf16(p[idx]);
+    } else {
+        const uint8_t *p = (const uint8_t *)(is_v ? pl->v_pool : pl->k_pool);
+        const float *sc = is_v ? pl->v_scale : pl->k_scale;
+        return oracle_e4m3_value(p[idx]) * (double)sc[page * pl->n_head_kv + kh];
+    }
+}
+
+/*
+ * Attention of one query vector over key positions 0..last of sequence seq,
+ * kv head kh.  Writes d doubles to out.  Returns 0, or -1 when a block-table
+ * entry that the row needs is outside the pool.
+ */
+static int orc_attend(const orc_pool *pl, const double *q, int seq, int64_t last, int kh,
+                      double *scores, double *out)
+{
+    const int d = pl->d, P = pl->P;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    int64_t t;
+    int i;
+    for (t = 0; t <= last; ++t) {
+        int64_t page = pl->block_table[(int64_t)seq * pl->max_pages + t / P];
+        double dot = 0.0;
+        if (page < 0 || page >= pl->n_pages)
+            return -1;
+        for (i = 0; i < d; ++i)
+            dot += q[i] * orc_elem(pl, 0, page, kh, (int)(t % P), i);
+        scores[t] = dot * inv_sqrt_d;
+    }
+    double mx = -INFINITY;
+    for (t = 0; t <= last; ++t)
+        if (scores[t] > mx)
+            mx = scores[t];
+    double z = 0.0;
+    for (t = 0; t <= last; ++t) {
+        scores[t] = exp(scores[t] - mx);
+        z += scores[t];
+    }
+    for (i = 0; i < d; ++i)
+        out[i] = 0.0;
+    for (t = 0; t <= last; ++t) {
+        int64_t page = pl->block_table[(int64_t)seq * pl->max_pages + t / P];
+        double w = scores[t] / z;
+        for (i = 0; i < d; ++i)
+            out[i] += w * orc_elem(pl, 1, page, kh, (int)(t % P), i);
+    }
+    return 0;
+}
+
+/*
+ * oracle_paged_attention -- every call shape at once.
+ *
+ *   q         bf16 bits [n_seq][rows][n_head][head_dim]
+ *   rows      R: 1 (decode), 8 (verify round), or the chunk length with
+ *             n_seq = 1 (prefill chunk)
+ *   ctx_lens  [n_seq] length of each sequence after this call
+ *   row_mask  [n_seq*rows] nonzero = compute that row, or NULL for all rows
+ *   out       fp64 [n_seq][rows][n_head][head_dim]; rows not computed are
+ *             left untouched
+ *
+ * Returns 0, -1 for a bad shape, -2 for a row whose context is shorter than
+ * the call's rows or longer than its block-table row, -3 for a block-table
+ * entry outside the pool.
+ */
+int oracle_paged_attention(const uint16_t *q, int n_seq, int rows,
+                           const void *k_pool, const void *v_pool,
+                           const float *k_scale, const float *v_scale, int64_t n_pages,
+                           const int32_t *block_table, int max_pages,
+                           const int32_t *ctx_lens, int n_head, int n_head_kv,
+                           int head_dim, int page_size, int kv_dtype,
+                           const uint8_t *row_mask, double *out, int n_threads)
+{
+    if (n_seq <= 0 || rows <= 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 ||
+        page_size <= 0 || n_head % n_head_kv != 0)
+        return -1;
+    orc_pool pl = {k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                   max_pages, n_head_kv, head_dim, page_size, kv_dtype};
+    const int g = n_head / n_head_kv;
+    int64_t max_ctx = 0;
+    for (int s = 0; s < n_seq; ++s) {
+        if (ctx_lens[s] < rows || (int64_t)ctx_lens[s] > (int64_t)max_pages * page_size)
+            return -2;
+        if (ctx_lens[s] > max_ctx)
+            max_ctx = ctx_lens[s];
+    }
+    const int64_t n_items = (int64_t)n_seq * rows * n_head;
+    int status = 0;
+    if (n_threads <= 0)
+        n_threads = 1;
+#pragma omp parallel num_threads(n_threads)
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)max_ctx);
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)head_dim);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < n_items; ++it) {
+            const int h = (int)(it % n_head);
+            const int64_t sr = it / n_head; /* s * rows + r */
+            const int r = (int)(sr % rows), s = (int)(sr / rows);
+            if (row_mask && !row_mask[sr])
+                continue;
+            const uint16_t *qv = q + it * head_dim;
+            for (int i = 0; i < head_dim; ++i)
+                qrow[i] = orc_bf16(qv[i]);
+            const int64_t last = (int64_t)ctx_lens[s] - rows + r;
+            if (orc_attend(&pl, qrow, s, last, h / g, scores, out + it * head_dim) != 0) {
+#pragma omp atomic write
+                status = -3;
+            }
+        }
+        free(scores);
+        free(qrow);
+    }
+    return status;
+}
+
+/* ---------------------------------------------------------------------- */
+/* fp8 quantisation                                                        */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Nearest E4M3 code to the fp32 value y, ties to the code with an even
+ * mantissa, magnitudes above the largest finite value (448) saturating to it.
+ * Plain search over the 127 non-negative finite codes, whose values increase
+ * with the code.
+ */
+uint8_t oracle_e4m3_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0; /* -0 keeps its sign, like any negative */
+    double a = fabs((double)y);
+    if (isnan(y))
+        return 0x7F;
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    int lo = 0, hi = 126; /* value(lo) <= a < value(hi) once narrowed */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (oracle_e4m3_value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double vlo = oracle_e4m3_value((uint8_t)lo), vhi = oracle_e4m3_value((uint8_t)hi);
+    int pick;
+    if (a - vlo < vhi - a)
+        pick = lo;
+    else if (a - vlo > vhi - a)
+        pick = hi;
+    else
+        pick = (lo & 1) ? hi : lo; /* tie: even code, i.e. even mantissa */
+    return (uint8_t)(sign | pick);
+}
+
+/*
+ * oracle_kv_append -- write n_tok new K/V rows into their token slots.
+ *
+ *   k_new, v_new  bf16 bits [n_tok][n_head_kv][head_dim]
+ *   slot_mapping  [n_tok] slot = page * page_size + offset ("kern manifest v7"
+ *                 schema, $defs.Fill "slot": a row's token slot in the paged
+ *                 state); a negative slot skips the row
+ *   pools         [n_pages][n_head_kv][page_size][head_dim], bf16 bits or
+ *                 E4M3 codes; scales fp32 [n_pages][n_head_kv] (fp8 only)
+ *
+ * bf16: a plain copy into the slot.
+ * fp8: one fp32 scale per (page, kv head), separately for K and for V, equal
+ * to absmax / 448 ("one fp32 scale per page per KV head (absmax/448)"), where
+ * absmax runs over every element of this call's rows that land in that page
+ * and head.  A page's scale is (re)set only by a call that writes the page's
+ * first slot (offset 0); a call that writes later slots of a page keeps the
+ * scale already stored and saturates.  A zero absmax gives scale 1.  Each
+ * element's code is the nearest E4M3 value to the fp32 quotient x / scale.
+ *
+ * Returns 0, or -1 for a slot outside the pool.
+ */
+int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new,
+                     const int32_t *slot_mapping, int n_tok,
+                     void *k_pool, void *v_pool, float *k_scale, float *v_scale,
+                     int64_t n_pages, int n_head_kv, int head_dim, int page_size,
+                     int kv_dtype)
+{
+    const int64_t row = (int64_t)n_head_kv * head_dim; /* elements per token */
+    for (int t = 0; t < n_tok; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot >= (int64_t)n_pages * page_size)
+            return -1;
+    }
+    if (kv_dtype == ORC_KV_BF16) {
+        for (int t = 0; t < n_tok; ++t) {
+            int64_t slot = slot_mapping[t];
+            if (slot < 0)
+                continue;
+            int64_t page = slot / page_size, off = slot % page_size;
+            for (int h = 0; h < n_head_kv; ++h)
+                for (int i = 0; i < head_dim; ++i) {
+                    int64_t dst = ((page * n_head_kv + h) * page_size + off) * head_dim + i;
+                    ((uint16_t *)k_pool)[dst] = k_new[t * row + (int64_t)h * head_dim + i];
+                    ((uint16_t *)v_pool)[dst] = v_new[t * row + (int64_t)h * head_dim + i];
+                }
+        }
+        return 0;
+    }
+    /* fp8: first the scales of pages whose first slot this call writes. */
+    for (int kv = 0; kv < 2; ++kv) {
+        const uint16_t *src = kv ? v_new : k_new;
+        float *scale = kv ? v_scale : k_scale;
+        for (int t = 0; t < n_tok; ++t) {
+            int64_t slot = slot_mapping[t];
+            if (slot < 0 || slot % page_size != 0)
+                continue;
+            int64_t page = slot / page_size;
+            for (int h = 0; h < n_head_kv; ++h) {
+                float absmax = 0.0f;
+                for (int u = 0; u < n_tok; ++u) {
+                    if (slot_mapping[u] < 0 || slot_mapping[u] / page_size != page)
+                        continue;
+                    for (int i = 0; i < head_dim; ++i) {
+                        float x = (float)orc_bf16(src[u * row + (int64_t)h * head_dim + i]);
+                        if (fabsf(x) > absmax)
+                            absmax = fabsf(x);
+                    }
+                }
+                scale[page * n_head_kv + h] = absmax > 0.0f ? absmax / 448.0f : 1.0f;
+            }
+        }
+    }
+    /* then every row's codes, with its page's scale. */
+    for (int kv = 0; kv < 2; ++kv) {
+        const uint16_t *src = kv ? v_new : k_new;
+        float *scale = kv ? v_scale : k_scale;
+        uint8_t *pool = (uint8_t *)(kv ? v_pool : k_pool);
+        for (int t = 0; t < n_tok; ++t) {
+            int64_t slot = slot_mapping[t];
+            if (slot < 0)
+                continue;
+            int64_t page = slot / page_size, off = slot % page_size;
+            for (int h = 0; h < n_head_kv; ++h) {
+                float sc = scale[page * n_head_kv + h];
+                for (int i = 0; i < head_dim; ++i) {
+                    float x = (float)orc_bf16(src[t * row + (int64_t)h * head_dim + i]);
+                    float y = x / sc;
+                    pool[((page * n_head_kv + h) * page_size + off) * head_dim + i] =
+                        oracle_e4m3_encode(y);
+                }
+            }
+        }
+    }
+    return 0;
+}
