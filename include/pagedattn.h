@@ -1,0 +1,253 @@
+/*
+ * pagedattn.h -- C ABI of a paged grouped-query attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * One operation in four call shapes: attention of a step's query rows over a
+ * paged K/V cache -- the decode step (many sequences, one row each), the
+ * speculative verify round (exactly eight rows per sequence, causal within
+ * the round), and the prefill chunk (one sequence, many rows) -- with a bf16
+ * or an fp8-e4m3 K/V cache, plus the append/quantise step that writes a
+ * call's new K/V rows into the cache and a host-side block-table builder.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless the argument name ends in `_host`.
+ *    The caller allocates and owns every buffer, including the workspace;
+ *    the library allocates no device memory and keeps no state between
+ *    calls apart from a per-thread error string and a per-device launch
+ *    shape it reads once from the driver.
+ *  - Device work is enqueued on `stream` and is asynchronous: inputs must
+ *    stay unchanged and outputs unread until the stream has passed the call.
+ *    Outputs never alias inputs.
+ *  - Return value: ATTN_OK, or a negative ATTN_E_* code.  Every argument the
+ *    host can see is checked before anything is enqueued; on error nothing
+ *    is written and attn_last_error() names the offending argument.  This
+ *    follows "Radiance Architecture Plugins -- declaring a model", section
+ *    "Step: issuing the graph": an op over zero rows is a shape error that
+ *    writes nothing, and a failing helper sets a named status.
+ *  - A shape or format the kernels do not serve returns ATTN_E_UNSUPPORTED;
+ *    there is never a silent fallback to another path (same page, section
+ *    "Probe: what the plugin measured": a switch that cannot be honoured is
+ *    refused, never substituted).
+ *  - head_dim is always an argument and is never computed from other sizes
+ *    (same page, section "Declare: the metadata").
+ *
+ * Device-resident inputs (lengths, block tables) cannot be checked on the
+ * host.  The kernels never read outside the buffers the sizes describe:
+ *  - a sequence whose ctx_len is below the call's rows or above
+ *    max_pages_per_seq * page_size gets NaN in every output element of its
+ *    rows;
+ *  - a block-table entry that a row needs and that lies outside
+ *    [0, n_pages) is not dereferenced, and the rows that need it get NaN.
+ * Callers that hold host copies may run attn_check_lengths_host() and
+ * attn_check_block_table_host() first for a named error instead.
+ *
+ * Data layout
+ * -----------
+ *   Q / out            bf16 [n_seq][rows][n_head][head_dim], rows = 1 for
+ *                      decode, 8 for verify; [n_rows][n_head][head_dim] for
+ *                      prefill.
+ *   k_pool / v_pool    [n_pages][n_head_kv][page_size][head_dim] of bf16, or
+ *                      of e4m3 codes (one byte each) for ATTN_KV_FP8_E4M3.
+ *                      One call covers one layer's pool.  The page count is
+ *                      the caller's ("kern manifest v7" schema,
+ *                      $defs.HostTensor: only the outermost extent is the
+ *                      host's choice).
+ *   k_scale / v_scale  fp32 [n_pages][n_head_kv]: one scale per page and kv
+ *                      head, separately for K and V (fp8 only; NULL for bf16).
+ *                      The stored value of element i is code_value * scale.
+ *   block_table        int32 [n_seq][max_pages_per_seq]; token t of sequence
+ *                      s lives in page block_table[s][t / page_size] at slot
+ *                      t % page_size ("kern manifest v7" schema, $defs.Domain:
+ *                      a block table whose index covers `stride` = 16 token
+ *                      slots).  Entries past a sequence's last page are
+ *                      never read.
+ *   ctx_lens           int32 [n_seq]: each sequence's length AFTER this call,
+ *                      i.e. the rows already cached plus this call's rows
+ *                      (same schema, $defs.Fill "seq_len").  The call's K/V
+ *                      must already be in the cache (attn_kv_append first).
+ *                      Row r of a call with R rows sits at position
+ *                      ctx_len - R + r and attends to keys 0 .. that position.
+ *
+ * Arithmetic: softmax(Q K^T / sqrt(head_dim)) V with fp32 accumulation,
+ * bf16 output rounded to nearest-even.  GQA: query head h reads kv head
+ * h / (n_head / n_head_kv).
+ *
+ * Determinism: decode and verify results depend only on the sequence's own
+ * inputs -- never on the batch size, the other sequences, the order of the
+ * batch or the device's compute-unit count -- and each verify row is bit for
+ * bit the decode result for the same position over the same cache
+ * ("TandemLLM -- Adding a model", section "The adapter path in ten steps",
+ * step 4: every verified row must equal the decode step's row bit for bit).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_KV_BF16 = 0, ATTN_KV_FP8_E4M3 = 1 } attn_kv_dtype;
+
+enum {
+    ATTN_OK = 0,
+    ATTN_E_ARG = -1,         /* null pointer, negative size, bad enum           */
+    ATTN_E_SHAPE = -2,       /* zero rows or sequences, heads not divisible ... */
+    ATTN_E_UNSUPPORTED = -3, /* head_dim / page size / group size not served    */
+    ATTN_E_WORKSPACE = -4,   /* workspace too small or misaligned               */
+    ATTN_E_RANGE = -5,       /* host-checked length or table entry out of range */
+    ATTN_E_DEVICE = -6       /* the HIP runtime refused a launch                */
+};
+
+/* Rows per sequence of a verify round: exact, not a bound ("kern manifest
+   v7" schema, $defs.Batch: rows is 1 for a decode step and 8 for a
+   speculative round). */
+#define ATTN_VERIFY_ROWS 8
+
+/* Page (block) size the kernels are built for.  The pages make the block
+   size a property of the attention kernel, read back by the engine
+   ("Radiance Architecture Plugins -- declaring a model", section "Declare:
+   buffers and KV groups"); the schema's block-table example uses 16. */
+#define ATTN_PAGE_SIZE 16
+
+/*
+ * attn_paged_decode -- one query row per sequence (decode step).
+ *
+ *   q          bf16 [n_seq][n_head][head_dim]
+ *   out        bf16 [n_seq][n_head][head_dim]
+ *   workspace  device scratch of at least
+ *              attn_paged_workspace_bytes(0, n_seq, max_pages_per_seq,
+ *              n_head, head_dim), 256-byte aligned; its contents are dead
+ *              between calls ("kern manifest v7" schema, $defs.BufferKind
+ *              "workspace").
+ * Other arguments as described in the header comment.  Needs
+ * n_head % n_head_kv == 0, n_head / n_head_kv <= 16, head_dim in {128, 256},
+ * page_size == ATTN_PAGE_SIZE, n_seq <= 4096.
+ */
+int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, int64_t n_pages,
+                      const int32_t* block_table, int32_t max_pages_per_seq,
+                      const int32_t* ctx_lens, int32_t n_seq, int32_t n_head,
+                      int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                      attn_kv_dtype kv_dtype, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_paged_verify -- exactly ATTN_VERIFY_ROWS query rows per sequence, the
+ * round's draft tokens, causal within the round and after the cached context.
+ *
+ *   q, out     bf16 [n_seq][ATTN_VERIFY_ROWS][n_head][head_dim]
+ *   workspace  attn_paged_workspace_bytes(1, ...)
+ * Row r of sequence s is at position ctx_lens[s] - 8 + r; its result equals,
+ * bit for bit, attn_paged_decode of that row with ctx_len = position + 1 over
+ * the same cache.  Needs ctx_lens[s] >= 8 and, besides the decode limits,
+ * ceil(8 / floor(16 / g)) * head_dim <= 512 with g = n_head / n_head_kv.
+ */
+int attn_paged_verify(const void* q, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, int64_t n_pages,
+                      const int32_t* block_table, int32_t max_pages_per_seq,
+                      const int32_t* ctx_lens, int32_t n_seq, int32_t n_head,
+                      int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                      attn_kv_dtype kv_dtype, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_paged_prefill -- a chunk of n_rows new rows of ONE sequence over its
+ * cached context ("kern manifest v7" schema, $defs.Batch: rows given by the
+ * chunk, one sequence; `context` is the cached rows it expands over).
+ *
+ *   q, out       bf16 [n_rows][n_head][head_dim]
+ *   block_table  int32 [max_pages_per_seq] (the sequence's row)
+ *   ctx_len      HOST value: the sequence's length after this call; row r is
+ *                at position ctx_len - n_rows + r.  Checked on the host:
+ *                n_rows <= ctx_len <= max_pages_per_seq * page_size.
+ *   workspace    attn_paged_workspace_bytes(2, ...) (may be 0 bytes)
+ * Needs n_head % n_head_kv == 0, head_dim in {128, 256}, kv_dtype bf16 or
+ * fp8 (fp8 pages are dequantised to bf16 in registers).
+ */
+int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const void* v_pool,
+                       const float* k_scale, const float* v_scale, int64_t n_pages,
+                       const int32_t* block_table, int32_t max_pages_per_seq, int32_t ctx_len,
+                       int32_t n_head, int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                       attn_kv_dtype kv_dtype, void* out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_kv_append -- write n_tok new K/V rows into their token slots
+ * ("kern manifest v7" schema, $defs.Fill "slot": each row's token slot in
+ * the paged state; slot = page * page_size + offset).  A negative slot skips
+ * its row (bucket padding).
+ *
+ *   k_new, v_new  bf16 [n_tok][n_head_kv][head_dim]
+ *   slot_mapping  int32 [n_tok]
+ * bf16 pools: a copy.  fp8 pools: a page's K scale and V scale are set to
+ * absmax / 448 (1 when absmax is 0) over this call's rows in that page, by
+ * the call that writes the page's offset 0; a call that writes only later
+ * offsets keeps the stored scale.  Each code is the E4M3 value nearest to
+ * the fp32 quotient x / scale, ties to even, saturating at +-448.
+ * Precondition for fp8: the rows a call writes into one page are adjacent
+ * in the call, in increasing offset order (true of any sequence's run of
+ * new tokens).  Slots must lie below n_pages * page_size; a larger slot
+ * skips its row.
+ */
+int attn_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                   int32_t n_tok, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                   int64_t n_pages, int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                   attn_kv_dtype kv_dtype, hipStream_t stream);
+
+/*
+ * attn_block_table_build -- HOST helper that deals each sequence its own
+ * pages from a pool of pool_pages pages.
+ *
+ * The pool's page ids are shuffled by a Fisher-Yates (Durstenfeld) pass
+ * driven by Vigna's splitmix64 seeded with `seed` (swap partner of position
+ * i = next() mod (i + 1), i from pool_pages-1 down to 1); sequence s, in
+ * order, then takes the next ceil(ctx_lens_host[s] / page_size) ids.
+ * Unused columns are -1.  If slot_mapping_host is not NULL it receives, for
+ * every sequence in order and every position t < ctx_lens_host[s], the slot
+ * block_table[s][t / page_size] * page_size + t % page_size.
+ * Returns ATTN_E_RANGE when a context needs more than max_pages_per_seq
+ * pages or the pool is too small.
+ */
+int attn_block_table_build(int32_t n_seq, const int32_t* ctx_lens_host, int32_t page_size,
+                           int64_t pool_pages, uint64_t seed, int32_t max_pages_per_seq,
+                           int32_t* block_table_host, int32_t* slot_mapping_host);
+
+/* op: 0 decode, 1 verify, 2 prefill.  Bytes of device workspace the call
+   needs; 0 for an unsupported combination. */
+size_t attn_paged_workspace_bytes(int op, int32_t n_seq, int32_t max_pages_per_seq,
+                                  int32_t n_head, int32_t head_dim);
+
+/* ATTN_OK if the kernels serve this (head_dim, page_size, kv_dtype),
+   else ATTN_E_UNSUPPORTED (the counterpart of the pages' probe bits). */
+int attn_caps(int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype);
+
+/* HOST checks of device-resident inputs, for callers holding host copies.
+   attn_check_lengths_host: rows <= ctx_lens[s] <= max_pages*page_size.
+   attn_check_block_table_host: every entry a sequence reads is in
+   [0, n_pages).  Return ATTN_OK or ATTN_E_RANGE (message names s). */
+int attn_check_lengths_host(const int32_t* ctx_lens_host, int32_t n_seq, int32_t rows,
+                            int32_t max_pages_per_seq, int32_t page_size);
+int attn_check_block_table_host(const int32_t* block_table_host, const int32_t* ctx_lens_host,
+                                int32_t n_seq, int32_t max_pages_per_seq, int32_t page_size,
+                                int64_t n_pages);
+
+/* Message of the last failing call on this thread ("" after a success). */
+const char* attn_last_error(void);
+
+/*
+ * Measurement hook: the next decode, verify or prefill call made on this
+ * thread records `start` just before and `stop` just after its main
+ * attention kernel, on the call's stream, then forgets both.  Pass NULLs to
+ * cancel.  Lets a benchmark time that kernel alone with HIP events.
+ */
+void attn_set_kernel_timer(hipEvent_t start, hipEvent_t stop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDATTN_H */

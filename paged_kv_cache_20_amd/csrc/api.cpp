@@ -1,0 +1,380 @@
+// api.cpp -- the C ABI declared in include/pagedattn.h: host-side argument
+// checks, error reporting, workspace sizing and dispatch to the kernels.
+//
+// Every check runs before anything is enqueued; a failing call writes
+// nothing and leaves a message naming the argument ("Radiance Architecture
+// Plugins -- declaring a model", section "Step: issuing the graph": zero rows
+// is a shape error that writes nothing; a failing helper sets a named
+// status).  Unserved shapes are refused, never routed elsewhere (same page,
+// section "Probe: what the plugin measured").
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pagedattn.h"
+#include "kernels.h"
+
+namespace pa {
+int split_tiles(int rows, int g);
+}
+
+namespace {
+
+thread_local char t_err[256] = "";
+thread_local hipEvent_t t_ev_start = nullptr;
+thread_local hipEvent_t t_ev_stop = nullptr;
+
+int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(t_err, sizeof t_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok()
+{
+    t_err[0] = 0;
+    return ATTN_OK;
+}
+
+int from_hip(hipError_t e, const char* what)
+{
+    if (e == hipSuccess)
+        return ok();
+    if (e == hipErrorNotSupported)
+        return fail(ATTN_E_UNSUPPORTED, "%s: shape not served by the kernels", what);
+    return fail(ATTN_E_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool head_dim_ok(int32_t d) { return d == 128 || d == 256; }
+
+// Checks common to decode / verify / prefill.  Returns ATTN_OK or a code.
+int check_common(const char* fn, const void* q, const void* k_pool, const void* v_pool,
+                 const float* k_scale, const float* v_scale, int64_t n_pages,
+                 const int32_t* block_table, int32_t max_pages, int32_t n_head,
+                 int32_t n_head_kv, int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype,
+                 const void* out)
+{
+    if (!q)
+        return fail(ATTN_E_ARG, "%s: q is NULL", fn);
+    if (!k_pool || !v_pool)
+        return fail(ATTN_E_ARG, "%s: k_pool/v_pool is NULL", fn);
+    if (!block_table)
+        return fail(ATTN_E_ARG, "%s: block_table is NULL", fn);
+    if (!out)
+        return fail(ATTN_E_ARG, "%s: out is NULL", fn);
+    if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3)
+        return fail(ATTN_E_ARG, "%s: kv_dtype %d is not a kv dtype", fn, (int)kv_dtype);
+    if (kv_dtype == ATTN_KV_FP8_E4M3 && (!k_scale || !v_scale))
+        return fail(ATTN_E_ARG, "%s: fp8 kv needs k_scale and v_scale", fn);
+    if (kv_dtype == ATTN_KV_BF16 && (k_scale || v_scale))
+        return fail(ATTN_E_ARG, "%s: bf16 kv takes no scales (pass NULL)", fn);
+    if (n_pages <= 0)
+        return fail(ATTN_E_SHAPE, "%s: n_pages must be positive (got %lld)", fn,
+                    (long long)n_pages);
+    if (n_pages > (int64_t)INT32_MAX)
+        return fail(ATTN_E_UNSUPPORTED, "%s: n_pages above 2^31-1", fn);
+    if (max_pages <= 0)
+        return fail(ATTN_E_SHAPE, "%s: max_pages_per_seq must be positive (got %d)", fn,
+                    max_pages);
+    if ((int64_t)max_pages * ATTN_PAGE_SIZE > (int64_t)INT32_MAX)
+        return fail(ATTN_E_UNSUPPORTED, "%s: max_pages_per_seq too large", fn);
+    if (n_head <= 0 || n_head_kv <= 0)
+        return fail(ATTN_E_SHAPE, "%s: n_head (%d) and n_head_kv (%d) must be positive", fn,
+                    n_head, n_head_kv);
+    if (n_head % n_head_kv != 0)
+        return fail(ATTN_E_SHAPE, "%s: n_head (%d) is not a multiple of n_head_kv (%d)", fn,
+                    n_head, n_head_kv);
+    if (head_dim <= 0)
+        return fail(ATTN_E_SHAPE, "%s: head_dim must be positive (got %d)", fn, head_dim);
+    if (!head_dim_ok(head_dim))
+        return fail(ATTN_E_UNSUPPORTED, "%s: head_dim %d not served (128, 256)", fn, head_dim);
+    if (page_size != ATTN_PAGE_SIZE)
+        return fail(ATTN_E_UNSUPPORTED, "%s: page_size %d not served (16)", fn, page_size);
+    return ATTN_OK;
+}
+
+int check_workspace(const char* fn, void* ws, size_t have, size_t need)
+{
+    if (need == 0)
+        return ATTN_OK;
+    if (!ws)
+        return fail(ATTN_E_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (((uintptr_t)ws & 255u) != 0)
+        return fail(ATTN_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    if (have < need)
+        return fail(ATTN_E_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, have, need);
+    return ATTN_OK;
+}
+
+size_t split_ws_bytes(int32_t rows, int32_t n_seq, int32_t max_pages, int32_t n_head,
+                      int32_t head_dim)
+{
+    const int64_t ms = pa::max_splits(max_pages, ATTN_PAGE_SIZE);
+    const int64_t rec = (int64_t)n_seq * ms * rows * n_head;
+    int64_t o_bytes = rec * head_dim * 4;
+    o_bytes = (o_bytes + 255) / 256 * 256;
+    return (size_t)(o_bytes + rec * 2 * 4);
+}
+
+int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
+               const void* v_pool, const float* k_scale, const float* v_scale, int64_t n_pages,
+               const int32_t* block_table, int32_t max_pages, const int32_t* ctx_lens,
+               int32_t n_seq, int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+               int32_t page_size, attn_kv_dtype kv_dtype, void* out, void* workspace,
+               size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                          max_pages, n_head, n_head_kv, head_dim, page_size, kv_dtype, out);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!ctx_lens)
+        return fail(ATTN_E_ARG, "%s: ctx_lens is NULL", fn);
+    if (n_seq <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero sequences is not a call (n_seq = %d)", fn, n_seq);
+    if (n_seq > pa::kMaxSeq)
+        return fail(ATTN_E_UNSUPPORTED, "%s: n_seq %d above %d", fn, n_seq, pa::kMaxSeq);
+    const int g = n_head / n_head_kv;
+    if (g > 16)
+        return fail(ATTN_E_UNSUPPORTED, "%s: %d query heads per kv head (at most 16)", fn, g);
+    const int nt = pa::split_tiles(rows, g);
+    if (nt * head_dim > 512)
+        return fail(ATTN_E_UNSUPPORTED,
+                    "%s: %d rows x %d heads per kv head at head_dim %d not served", fn, rows, g,
+                    head_dim);
+    const size_t need = split_ws_bytes(rows, n_seq, max_pages, n_head, head_dim);
+    rc = check_workspace(fn, workspace, workspace_bytes, need);
+    if (rc != ATTN_OK)
+        return rc;
+
+    pa::SplitArgs a;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.n_pages = n_pages;
+    a.block_table = block_table;
+    a.max_pages = max_pages;
+    a.ctx_lens = ctx_lens;
+    a.n_seq = n_seq;
+    a.n_head = n_head;
+    a.n_head_kv = n_head_kv;
+    a.head_dim = head_dim;
+    a.rows = rows;
+    a.fp8 = kv_dtype == ATTN_KV_FP8_E4M3;
+    a.out = out;
+    a.max_split = (int32_t)pa::max_splits(max_pages, ATTN_PAGE_SIZE);
+    const int64_t rec = (int64_t)n_seq * a.max_split * rows * n_head;
+    const int64_t o_bytes = (rec * head_dim * 4 + 255) / 256 * 256;
+    a.o_part = (float*)workspace;
+    a.ml_part = (float*)((char*)workspace + o_bytes);
+    a.ev_start = t_ev_start;
+    a.ev_stop = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    return from_hip(pa::launch_split_decode(a, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return t_err; }
+
+void attn_set_kernel_timer(hipEvent_t start, hipEvent_t stop)
+{
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+
+int attn_caps(int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype)
+{
+    if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3)
+        return fail(ATTN_E_UNSUPPORTED, "attn_caps: kv_dtype %d unknown", (int)kv_dtype);
+    if (!head_dim_ok(head_dim))
+        return fail(ATTN_E_UNSUPPORTED, "attn_caps: head_dim %d not served", head_dim);
+    if (page_size != ATTN_PAGE_SIZE)
+        return fail(ATTN_E_UNSUPPORTED, "attn_caps: page_size %d not served", page_size);
+    return ok();
+}
+
+size_t attn_paged_workspace_bytes(int op, int32_t n_seq, int32_t max_pages_per_seq,
+                                  int32_t n_head, int32_t head_dim)
+{
+    if (n_seq <= 0 || max_pages_per_seq <= 0 || n_head <= 0 || !head_dim_ok(head_dim))
+        return 0;
+    switch (op) {
+    case 0: return split_ws_bytes(1, n_seq, max_pages_per_seq, n_head, head_dim);
+    case 1: return split_ws_bytes(ATTN_VERIFY_ROWS, n_seq, max_pages_per_seq, n_head, head_dim);
+    case 2: return 0;
+    default: return 0;
+    }
+}
+
+int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, int64_t n_pages,
+                      const int32_t* block_table, int32_t max_pages_per_seq,
+                      const int32_t* ctx_lens, int32_t n_seq, int32_t n_head,
+                      int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                      attn_kv_dtype kv_dtype, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream)
+{
+    return split_call("attn_paged_decode", 1, q, k_pool, v_pool, k_scale, v_scale, n_pages,
+                      block_table, max_pages_per_seq, ctx_lens, n_seq, n_head, n_head_kv,
+                      head_dim, page_size, kv_dtype, out, workspace, workspace_bytes, stream);
+}
+
+int attn_paged_verify(const void* q, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, int64_t n_pages,
+                      const int32_t* block_table, int32_t max_pages_per_seq,
+                      const int32_t* ctx_lens, int32_t n_seq, int32_t n_head,
+                      int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                      attn_kv_dtype kv_dtype, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream)
+{
+    return split_call("attn_paged_verify", ATTN_VERIFY_ROWS, q, k_pool, v_pool, k_scale,
+                      v_scale, n_pages, block_table, max_pages_per_seq, ctx_lens, n_seq, n_head,
+                      n_head_kv, head_dim, page_size, kv_dtype, out, workspace, workspace_bytes,
+                      stream);
+}
+
+int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const void* v_pool,
+                       const float* k_scale, const float* v_scale, int64_t n_pages,
+                       const int32_t* block_table, int32_t max_pages_per_seq, int32_t ctx_len,
+                       int32_t n_head, int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                       attn_kv_dtype kv_dtype, void* out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream)
+{
+    const char* fn = "attn_paged_prefill";
+    int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                          max_pages_per_seq, n_head, n_head_kv, head_dim, page_size, kv_dtype,
+                          out);
+    if (rc != ATTN_OK)
+        return rc;
+    if (n_rows <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (n_rows = %d)", fn, n_rows);
+    if (ctx_len < n_rows)
+        return fail(ATTN_E_RANGE, "%s: ctx_len %d is below n_rows %d", fn, ctx_len, n_rows);
+    if ((int64_t)ctx_len > (int64_t)max_pages_per_seq * page_size)
+        return fail(ATTN_E_RANGE, "%s: ctx_len %d exceeds max_pages_per_seq * page_size", fn,
+                    ctx_len);
+    (void)workspace;
+    (void)workspace_bytes;
+    pa::PrefillArgs a;
+    a.q = q;
+    a.n_rows = n_rows;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.n_pages = n_pages;
+    a.block_table = block_table;
+    a.max_pages = max_pages_per_seq;
+    a.ctx_len = ctx_len;
+    a.n_head = n_head;
+    a.n_head_kv = n_head_kv;
+    a.head_dim = head_dim;
+    a.fp8 = kv_dtype == ATTN_KV_FP8_E4M3;
+    a.out = out;
+    a.ev_start = t_ev_start;
+    a.ev_stop = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    return from_hip(pa::launch_prefill(a, stream), fn);
+}
+
+int attn_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                   int32_t n_tok, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                   int64_t n_pages, int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                   attn_kv_dtype kv_dtype, hipStream_t stream)
+{
+    const char* fn = "attn_kv_append";
+    if (!k_new || !v_new)
+        return fail(ATTN_E_ARG, "%s: k_new/v_new is NULL", fn);
+    if (!slot_mapping)
+        return fail(ATTN_E_ARG, "%s: slot_mapping is NULL", fn);
+    if (!k_pool || !v_pool)
+        return fail(ATTN_E_ARG, "%s: k_pool/v_pool is NULL", fn);
+    if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3)
+        return fail(ATTN_E_ARG, "%s: kv_dtype %d is not a kv dtype", fn, (int)kv_dtype);
+    if (kv_dtype == ATTN_KV_FP8_E4M3 && (!k_scale || !v_scale))
+        return fail(ATTN_E_ARG, "%s: fp8 kv needs k_scale and v_scale", fn);
+    if (kv_dtype == ATTN_KV_BF16 && (k_scale || v_scale))
+        return fail(ATTN_E_ARG, "%s: bf16 kv takes no scales (pass NULL)", fn);
+    if (n_tok <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (n_tok = %d)", fn, n_tok);
+    if (n_pages <= 0)
+        return fail(ATTN_E_SHAPE, "%s: n_pages must be positive", fn);
+    if (n_head_kv <= 0 || head_dim <= 0)
+        return fail(ATTN_E_SHAPE, "%s: n_head_kv and head_dim must be positive", fn);
+    if (!head_dim_ok(head_dim))
+        return fail(ATTN_E_UNSUPPORTED, "%s: head_dim %d not served (128, 256)", fn, head_dim);
+    if (page_size != ATTN_PAGE_SIZE)
+        return fail(ATTN_E_UNSUPPORTED, "%s: page_size %d not served (16)", fn, page_size);
+    if (n_head_kv > 65535)
+        return fail(ATTN_E_UNSUPPORTED, "%s: n_head_kv above 65535", fn);
+    pa::AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slots = slot_mapping;
+    a.n_tok = n_tok;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.n_pages = n_pages;
+    a.n_head_kv = n_head_kv;
+    a.head_dim = head_dim;
+    a.fp8 = kv_dtype == ATTN_KV_FP8_E4M3;
+    return from_hip(pa::launch_append(a, stream), fn);
+}
+
+int attn_check_lengths_host(const int32_t* ctx_lens_host, int32_t n_seq, int32_t rows,
+                            int32_t max_pages_per_seq, int32_t page_size)
+{
+    const char* fn = "attn_check_lengths_host";
+    if (!ctx_lens_host)
+        return fail(ATTN_E_ARG, "%s: ctx_lens_host is NULL", fn);
+    if (n_seq <= 0 || rows <= 0)
+        return fail(ATTN_E_SHAPE, "%s: n_seq and rows must be positive", fn);
+    const int64_t cap = (int64_t)max_pages_per_seq * page_size;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        if (ctx_lens_host[s] < rows)
+            return fail(ATTN_E_RANGE, "%s: ctx_lens[%d] = %d is below the call's %d rows", fn, s,
+                        ctx_lens_host[s], rows);
+        if ((int64_t)ctx_lens_host[s] > cap)
+            return fail(ATTN_E_RANGE, "%s: ctx_lens[%d] = %d exceeds %lld slots", fn, s,
+                        ctx_lens_host[s], (long long)cap);
+    }
+    return ok();
+}
+
+int attn_check_block_table_host(const int32_t* block_table_host, const int32_t* ctx_lens_host,
+                                int32_t n_seq, int32_t max_pages_per_seq, int32_t page_size,
+                                int64_t n_pages)
+{
+    const char* fn = "attn_check_block_table_host";
+    if (!block_table_host || !ctx_lens_host)
+        return fail(ATTN_E_ARG, "%s: NULL argument", fn);
+    if (n_seq <= 0 || max_pages_per_seq <= 0 || page_size <= 0)
+        return fail(ATTN_E_SHAPE, "%s: sizes must be positive", fn);
+    for (int32_t s = 0; s < n_seq; ++s) {
+        const int64_t c = ctx_lens_host[s] < 0 ? 0 : ctx_lens_host[s];
+        int64_t need = (c + page_size - 1) / page_size;
+        if (need > max_pages_per_seq)
+            return fail(ATTN_E_RANGE, "%s: sequence %d needs %lld pages, row holds %d", fn, s,
+                        (long long)need, max_pages_per_seq);
+        for (int64_t i = 0; i < need; ++i) {
+            const int32_t p = block_table_host[(int64_t)s * max_pages_per_seq + i];
+            if (p < 0 || (int64_t)p >= n_pages)
+                return fail(ATTN_E_RANGE, "%s: block_table[%d][%lld] = %d outside [0, %lld)", fn,
+                            s, (long long)i, p, (long long)n_pages);
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// kernels.h -- launchers shared between the C-ABI layer (api.cpp) and the
+// HIP kernel sources.  Internal; not installed.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Tokens per split of the split-K decode/verify kernel.  Split boundaries sit
+// at absolute multiples of this value, so a row's partial results depend only
+// on its own position and context -- never on batch size or row count.
+constexpr int kChunk = 512;
+// Largest batch the decode/verify kernels take (the per-block prefix over
+// sequences lives in LDS).
+constexpr int kMaxSeq = 4096;
+
+inline int64_t max_splits(int32_t max_pages_per_seq, int32_t page_size)
+{
+    return ((int64_t)max_pages_per_seq * page_size + kChunk - 1) / kChunk;
+}
+
+struct SplitArgs {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const float* k_scale;
+    const float* v_scale;
+    int64_t n_pages;
+    const int32_t* block_table;
+    int32_t max_pages;
+    const int32_t* ctx_lens;
+    int32_t n_seq, n_head, n_head_kv, head_dim, rows;
+    int fp8;
+    void* out;
+    float* o_part;   // [n_seq][max_split][rows][n_head][head_dim]
+    float* ml_part;  // [n_seq][max_split][rows][n_head][2]
+    int32_t max_split;
+    hipEvent_t ev_start, ev_stop;  // optional timing pair around the split kernel
+};
+
+// Decode (rows = 1) and verify (rows = 8): split kernel + fixed-order combine.
+hipError_t launch_split_decode(const SplitArgs& a, hipStream_t stream);
+
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    const int32_t* slots;
+    int32_t n_tok;
+    void* k_pool;
+    void* v_pool;
+    float* k_scale;
+    float* v_scale;
+    int64_t n_pages;
+    int32_t n_head_kv, head_dim;
+    int fp8;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+    const void* q;
+    int32_t n_rows;
+    const void* k_pool;
+    const void* v_pool;
+    const float* k_scale;
+    const float* v_scale;
+    int64_t n_pages;
+    const int32_t* block_table;
+    int32_t max_pages;
+    int32_t ctx_len;
+    int32_t n_head, n_head_kv, head_dim;
+    int fp8;
+    void* out;
+    hipEvent_t ev_start, ev_stop;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa
