@@ -73,6 +73,19 @@ double oracle_e4m3_value(uint8_t c)
     return sign ? -v : v;
 }
 
+/* Values of all 256 codes, filled from oracle_e4m3_value before use. */
+static double orc_e4m3_tab[256];
+static int orc_e4m3_tab_ready = 0;
+
+static void orc_e4m3_init(void)
+{
+    if (orc_e4m3_tab_ready)
+        return;
+    for (int c = 0; c < 256; ++c)
+        orc_e4m3_tab[c] = oracle_e4m3_value((uint8_t)c);
+    orc_e4m3_tab_ready = 1;
+}
+
 typedef struct {
     const void *k_pool, *v_pool;
     const float *k_scale, *v_scale;
@@ -91,7 +104,7 @@ static double orc_elem(const orc_pool *pl, int is_v, int64_t page, int kh, int o
     } else {
         const uint8_t *p = (const uint8_t *)(is_v ? pl->v_pool : pl->k_pool);
         const float *sc = is_v ? pl->v_scale : pl->k_scale;
-        return oracle_e4m3_value(p[idx]) * (double)sc[page * pl->n_head_kv + kh];
+        return orc_e4m3_tab[p[idx]] * (double)sc[page * pl->n_head_kv + kh];
     }
 }
 
@@ -162,6 +175,7 @@ int oracle_paged_attention(const uint16_t *q, int n_seq, int rows,
     if (n_seq <= 0 || rows <= 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 ||
         page_size <= 0 || n_head % n_head_kv != 0)
         return -1;
+    orc_e4m3_init();
     orc_pool pl = {k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                    max_pages, n_head_kv, head_dim, page_size, kv_dtype};
     const int g = n_head / n_head_kv;
@@ -220,15 +234,16 @@ uint8_t oracle_e4m3_encode(float y)
         return 0x7F;
     if (a >= 448.0)
         return (uint8_t)(sign | 0x7E);
+    orc_e4m3_init();
     int lo = 0, hi = 126; /* value(lo) <= a < value(hi) once narrowed */
     while (hi - lo > 1) {
         int mid = (lo + hi) / 2;
-        if (oracle_e4m3_value((uint8_t)mid) <= a)
+        if (orc_e4m3_tab[mid] <= a)
             lo = mid;
         else
             hi = mid;
     }
-    double vlo = oracle_e4m3_value((uint8_t)lo), vhi = oracle_e4m3_value((uint8_t)hi);
+    double vlo = orc_e4m3_tab[lo], vhi = orc_e4m3_tab[hi];
     int pick;
     if (a - vlo < vhi - a)
         pick = lo;
@@ -287,29 +302,40 @@ int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new,
         }
         return 0;
     }
-    /* fp8: first the scales of pages whose first slot this call writes. */
-    for (int kv = 0; kv < 2; ++kv) {
-        const uint16_t *src = kv ? v_new : k_new;
-        float *scale = kv ? v_scale : k_scale;
-        for (int t = 0; t < n_tok; ++t) {
-            int64_t slot = slot_mapping[t];
-            if (slot < 0 || slot % page_size != 0)
-                continue;
-            int64_t page = slot / page_size;
-            for (int h = 0; h < n_head_kv; ++h) {
-                float absmax = 0.0f;
-                for (int u = 0; u < n_tok; ++u) {
-                    if (slot_mapping[u] < 0 || slot_mapping[u] / page_size != page)
-                        continue;
+    /* fp8: first the scales of pages whose first slot this call writes:
+       mark those pages, take absmax over every row of the call that lands in
+       a marked page, then store absmax / 448 (1 for a zero absmax). */
+    {
+        uint8_t *reset = (uint8_t *)calloc((size_t)n_pages, 1);
+        float *amax = (float *)calloc((size_t)(n_pages * n_head_kv), sizeof(float));
+        for (int t = 0; t < n_tok; ++t)
+            if (slot_mapping[t] >= 0 && slot_mapping[t] % page_size == 0)
+                reset[slot_mapping[t] / page_size] = 1;
+        for (int kv = 0; kv < 2; ++kv) {
+            const uint16_t *src = kv ? v_new : k_new;
+            float *scale = kv ? v_scale : k_scale;
+            memset(amax, 0, sizeof(float) * (size_t)(n_pages * n_head_kv));
+            for (int t = 0; t < n_tok; ++t) {
+                int64_t slot = slot_mapping[t];
+                if (slot < 0 || !reset[slot / page_size])
+                    continue;
+                int64_t page = slot / page_size;
+                for (int h = 0; h < n_head_kv; ++h)
                     for (int i = 0; i < head_dim; ++i) {
-                        float x = (float)orc_bf16(src[u * row + (int64_t)h * head_dim + i]);
-                        if (fabsf(x) > absmax)
-                            absmax = fabsf(x);
+                        float x = fabsf((float)orc_bf16(src[t * row + (int64_t)h * head_dim + i]));
+                        if (x > amax[page * n_head_kv + h])
+                            amax[page * n_head_kv + h] = x;
                     }
-                }
-                scale[page * n_head_kv + h] = absmax > 0.0f ? absmax / 448.0f : 1.0f;
             }
+            for (int64_t page = 0; page < n_pages; ++page)
+                if (reset[page])
+                    for (int h = 0; h < n_head_kv; ++h) {
+                        float a = amax[page * n_head_kv + h];
+                        scale[page * n_head_kv + h] = a > 0.0f ? a / 448.0f : 1.0f;
+                    }
         }
+        free(reset);
+        free(amax);
     }
     /* then every row's codes, with its page's scale. */
     for (int kv = 0; kv < 2; ++kv) {
