@@ -1,0 +1,387 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-secondary] [--no-cpu]
+
+Prints ONE JSON line.  The headline workload is the fp8-KV decode step at
+256 sequences (n_head 32, n_head_kv 8, head_dim 128, page 16, contexts
+log-uniform in [2048, 32768]); one step is the append/quantise of each
+sequence's newest K/V row followed by the decode attention call.  `value` is
+the step's algorithmic HBM bytes divided by its wall time (inputs resident in
+HBM).  `roofline` times the split-K attention kernel alone with HIP events
+(recorded by the library on the call's stream) and prices its algorithmic
+bytes against 8 TB/s.  `secondary` times the other workloads the same way:
+single-sequence decode (latency), 64-sequence bf16 decode at head_dim 256,
+the 8-row verify round, and the 4096-row prefill chunk (bf16 MFMA TFLOP/s).
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the headline
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk, dense
+METRIC = "paged-attn decode µs/step & HBM GB/s (% peak) at 256 seqs; prefill MFMA TFLOP/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime (torch's events only see
+    torch's own streams)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.hip.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def decode_bytes(lengths, w, with_out=True):
+    """Algorithmic bytes of one decode/verify call: K and V of every cached
+    token of every kv head (1 byte per element for fp8, 2 for bf16), the fp8
+    scales and block-table entries of every page read, Q, the lengths, and
+    (with_out) the output."""
+    b = 1 if w.kv_fp8 else 2
+    tot = 0
+    for c in lengths:
+        pages = -(-c // 16)
+        tot += c * w.n_head_kv * w.head_dim * 2 * b + pages * 4
+        if w.kv_fp8:
+            tot += pages * w.n_head_kv * 2 * 4
+    q = w.n_seq * w.rows * w.n_head * w.head_dim * 2
+    tot += q + 4 * w.n_seq + (q if with_out else 0)
+    return tot
+
+
+def append_bytes(n_tok, w):
+    """Append of n_tok rows: bf16 K and V read, stored K and V written, the
+    slot list, and (fp8) the page scales read."""
+    e = n_tok * w.n_head_kv * w.head_dim
+    return e * 2 * 2 + e * 2 * (1 if w.kv_fp8 else 2) + 4 * n_tok + \
+        (n_tok * w.n_head_kv * 2 * 4 if w.kv_fp8 else 0)
+
+
+def prefill_flops(n_rows, ctx, w):
+    """4 * n_head * head_dim per (row, key) pair the causal mask admits."""
+    cached = ctx - n_rows
+    pairs = n_rows * cached + n_rows * (n_rows + 1) // 2
+    return 4 * w.n_head * w.head_dim * pairs
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "prefill.hip", "append.hip"):
+        with open(os.path.join(ROOT, "paged_kv_cache_20_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, torch, pa, synth):
+        self.torch, self.pa, self.synth = torch, pa, synth
+        self.ev = HipEvents()
+
+    def setup_split(self, name):
+        torch, pa, synth = self.torch, self.pa, self.synth
+        w = synth.WORKLOADS[name]
+        inp = synth.draw(w, "cuda")
+        k, v, ks, vs = synth.poison_pools(inp.n_pages, w, "cuda")
+        kv = pa.KV_FP8_E4M3 if w.kv_fp8 else pa.KV_BF16
+        pa.attn_kv_append(inp.k_src, inp.v_src, inp.slots, inp.slots.numel(), k, v, ks, vs,
+                          inp.n_pages, w.n_head_kv, w.head_dim, 16, kv)
+        op = {"decode": 0, "verify": 1}[w.kind]
+        wsb = pa.attn_paged_workspace_bytes(op, w.n_seq, w.max_pages, w.n_head, w.head_dim)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(inp.q)
+        # the step's own new rows: the last `rows` tokens of every sequence
+        lens = inp.lengths.to(torch.int64)
+        ends = torch.cumsum(lens, 0)
+        idx = torch.cat([torch.arange(int(e) - w.rows, int(e), device="cuda") for e in ends])
+        st = dict(w=w, inp=inp, k=k, v=v, ks=ks, vs=vs, kv=kv, ws=ws, wsb=wsb, out=out,
+                  k_new=inp.k_src[idx].contiguous(), v_new=inp.v_src[idx].contiguous(),
+                  slots_new=inp.slots[idx].contiguous(),
+                  lengths_host=inp.lengths.cpu().tolist())
+        torch.cuda.synchronize()
+        return st
+
+    def split_step(self, st, timer=None):
+        pa = self.pa
+        w, inp = st["w"], st["inp"]
+        pa.attn_kv_append(st["k_new"], st["v_new"], st["slots_new"], st["slots_new"].numel(),
+                          st["k"], st["v"], st["ks"], st["vs"], inp.n_pages, w.n_head_kv,
+                          w.head_dim, 16, st["kv"])
+        if timer is not None:
+            pa.attn_set_kernel_timer(timer[0], timer[1])
+        fn = pa.attn_paged_decode if w.kind == "decode" else pa.attn_paged_verify
+        fn(inp.q, st["k"], st["v"], st["ks"], st["vs"], inp.n_pages, inp.table, w.max_pages,
+           inp.lengths, w.n_seq, w.n_head, w.n_head_kv, w.head_dim, 16, st["kv"], st["out"],
+           st["ws"], st["wsb"])
+
+    def time_split(self, st, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.split_step(st)
+        torch.cuda.synchronize()
+        evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.split_step(st, evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        kern = [self.ev.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            self.ev.destroy(a)
+            self.ev.destroy(b)
+        return wall, sum(kern) / len(kern), sorted(kern)[len(kern) // 2]
+
+    def setup_prefill(self, name):
+        torch, pa, synth = self.torch, self.pa, self.synth
+        w = synth.WORKLOADS[name]
+        inp = synth.draw(w, "cuda")
+        k, v, ks, vs = synth.poison_pools(inp.n_pages, w, "cuda")
+        kv = pa.KV_FP8_E4M3 if w.kv_fp8 else pa.KV_BF16
+        pa.attn_kv_append(inp.k_src, inp.v_src, inp.slots, inp.slots.numel(), k, v, ks, vs,
+                          inp.n_pages, w.n_head_kv, w.head_dim, 16, kv)
+        out = torch.empty((w.rows, w.n_head, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        C = int(inp.lengths[0])
+        st = dict(w=w, inp=inp, k=k, v=v, ks=ks, vs=vs, kv=kv, out=out, C=C,
+                  q=inp.q.view(w.rows, w.n_head, w.head_dim),
+                  k_new=inp.k_src[C - w.rows:].contiguous(),
+                  v_new=inp.v_src[C - w.rows:].contiguous(),
+                  slots_new=inp.slots[C - w.rows:].contiguous())
+        torch.cuda.synchronize()
+        return st
+
+    def prefill_step(self, st, timer=None):
+        pa = self.pa
+        w, inp = st["w"], st["inp"]
+        pa.attn_kv_append(st["k_new"], st["v_new"], st["slots_new"], w.rows, st["k"], st["v"],
+                          st["ks"], st["vs"], inp.n_pages, w.n_head_kv, w.head_dim, 16, st["kv"])
+        if timer is not None:
+            pa.attn_set_kernel_timer(timer[0], timer[1])
+        pa.attn_paged_prefill(st["q"], w.rows, st["k"], st["v"], st["ks"], st["vs"],
+                              inp.n_pages, inp.table, w.max_pages, st["C"], w.n_head,
+                              w.n_head_kv, w.head_dim, 16, st["kv"], st["out"])
+
+    def time_prefill(self, st, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.prefill_step(st)
+        torch.cuda.synchronize()
+        evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.prefill_step(st, evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        kern = [self.ev.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            self.ev.destroy(a)
+            self.ev.destroy(b)
+        return wall, sum(kern) / len(kern), sorted(kern)[len(kern) // 2]
+
+
+def cpu_baseline(st, torch, synth, budget_tokens=400_000):
+    """The CPU oracle timed on the first sequences of the headline workload
+    (up to `budget_tokens` cached tokens), priced with the same byte
+    accounting as the GPU value."""
+    import numpy as np
+    import oracle
+
+    w, inp = st["w"], st["inp"]
+    lens = st["lengths_host"]
+    n, tot = 0, 0
+    while n < len(lens) and tot + lens[n] <= budget_tokens:
+        tot += lens[n]
+        n += 1
+    n = max(n, 1)
+    need = [-(-c // 16) for c in lens[:n]]
+    table = inp.table[:n].cpu().numpy()
+    old = np.concatenate([table[s, :k] for s, k in enumerate(need)])
+    new_table = np.full((n, w.max_pages), -1, np.int32)
+    pos = 0
+    for s, k in enumerate(need):
+        new_table[s, :k] = np.arange(pos, pos + k)
+        pos += k
+    idx = torch.from_numpy(old.astype(np.int64)).cuda()
+    kp = synth.bits(st["k"].index_select(0, idx))
+    vp = synth.bits(st["v"].index_select(0, idx))
+    ks = st["ks"].index_select(0, idx).cpu().numpy() if w.kv_fp8 else None
+    vs = st["vs"].index_select(0, idx).cpu().numpy() if w.kv_fp8 else None
+    q = synth.bits(inp.q[:n])
+    threads = oracle.default_threads()
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.paged_attention(q, kp, vp, new_table, np.asarray(lens[:n], np.int32),
+                           n_head=w.n_head, n_head_kv=w.n_head_kv, head_dim=w.head_dim,
+                           page_size=16, kv_dtype=oracle.KV_FP8 if w.kv_fp8 else oracle.KV_BF16,
+                           k_scale=ks, v_scale=vs, threads=threads)
+    dt = time.perf_counter() - t0
+    sub = synth.scaled(w, n_seq=n)
+    gbs = decode_bytes(lens[:n], sub) / dt / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "decode attention of the first %d of 256 sequences (%d cached tokens, "
+                      "fp64 oracle, %.1f s)" % (n, tot, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_256seq_fp8")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_20_amd as pa
+    from paged_kv_cache_20_amd import synth
+
+    torch.cuda.set_device(0)
+    b = Bench(torch, pa, synth)
+    name = args.workload
+    w = synth.WORKLOADS[name]
+    log("[bench] headline", name)
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16", "data": "synthetic"}
+    if w.kind == "prefill":
+        st = b.setup_prefill(name)
+        wall, kavg, kmed = b.time_prefill(st, args.steps, args.warmup)
+        fl = prefill_flops(w.rows, st["C"], w)
+        result.update(value=round(fl / wall / 1e12, 2), unit="TFLOP/s",
+                      ms_per_step=round(wall * 1e3, 4))
+        achieved = fl / (kavg * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
+                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                              "traffic": traffic_from_profiles("prefill_kernel")}
+    else:
+        st = b.setup_split(name)
+        wall, kavg, kmed = b.time_split(st, args.steps, args.warmup)
+        lens = st["lengths_host"]
+        step_bytes = decode_bytes(lens, w) + append_bytes(w.n_seq * w.rows, w)
+        split_bytes = decode_bytes(lens, w, with_out=False)
+        result.update(value=round(step_bytes / wall / 1e9, 2), unit="GB/s",
+                      ms_per_step=round(wall * 1e3, 4))
+        achieved = split_bytes / (kavg * 1e-3) / 1e9
+        result["us_per_step"] = round(wall * 1e6, 2)
+        result["hbm_frac"] = round(step_bytes / wall / 1e9 / HBM_PEAK_GBS, 4)
+        result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBS, 4),
+                              "traffic": traffic_from_profiles("split_kernel_" + name),
+                              "kernel": "split_kernel", "kernel_avg_us": round(kavg * 1e3, 2),
+                              "kernel_median_us": round(kmed * 1e3, 2),
+                              "algorithmic_bytes_per_launch": split_bytes}
+    result["config"] = {"workload": name, "n_seq": w.n_seq, "rows": w.rows, "n_head": w.n_head,
+                        "n_head_kv": w.n_head_kv, "head_dim": w.head_dim, "page_size": 16,
+                        "kv_dtype": "fp8-e4m3" if w.kv_fp8 else "bf16",
+                        "ctx": "%s[%d,%d]" % (w.lengths, w.ctx_lo, w.ctx_hi),
+                        "sum_ctx": int(sum(st["inp"].lengths.cpu().tolist())),
+                        "seed": w.seed}
+    log("[bench] headline done", json.dumps(result))
+
+    if not args.no_cpu and w.kind != "prefill":
+        log("[bench] cpu baseline")
+        result["cpu_baseline"] = cpu_baseline(st, torch, synth)
+        log("[bench] cpu baseline done", result["cpu_baseline"])
+    del st
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        for other in ("decode_1seq_ctx512", "decode_64seq_hd256", "verify_32seq_8rows",
+                      "prefill_4096_over_28672"):
+            if other == name:
+                continue
+            ow = synth.WORKLOADS[other]
+            log("[bench] secondary", other)
+            try:
+                if ow.kind == "prefill":
+                    s2 = b.setup_prefill(other)
+                    wall, kavg, kmed = b.time_prefill(s2, 10, 3)
+                    fl = prefill_flops(ow.rows, s2["C"], ow)
+                    sec[other] = {"ms_per_step": round(wall * 1e3, 4),
+                                  "kernel_avg_ms": round(kavg, 4),
+                                  "tflops": round(fl / (kavg * 1e-3) / 1e12, 2),
+                                  "mfma_frac": round(fl / (kavg * 1e-3) / 1e12 /
+                                                     BF16_MFMA_PEAK_TFLOPS, 4),
+                                  "flops_per_launch": fl}
+                else:
+                    s2 = b.setup_split(other)
+                    wall, kavg, kmed = b.time_split(s2, 30, 5)
+                    lens = s2["lengths_host"]
+                    by = decode_bytes(lens, ow, with_out=False)
+                    sec[other] = {"us_per_step": round(wall * 1e6, 2),
+                                  "kernel_avg_us": round(kavg * 1e3, 2),
+                                  "kernel_gbs": round(by / (kavg * 1e-3) / 1e9, 1),
+                                  "hbm_frac": round(by / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "bytes_per_launch": by}
+                    if ow.kind == "verify":
+                        fl = 4 * ow.n_head * ow.head_dim * sum(
+                            8 * c - 28 for c in lens)  # pairs of 8 causal rows
+                        sec[other]["tflops"] = round(fl / (kavg * 1e-3) / 1e12, 2)
+                del s2
+            except Exception as e:  # report, keep the headline
+                sec[other] = {"error": str(e)[:200]}
+            torch.cuda.empty_cache()
+            log("[bench] secondary done", other, sec[other])
+        result["secondary"] = sec
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
