@@ -9,20 +9,23 @@
 //   consecutive positions x the g query heads that share the kv head, so
 //   every K/V tile it stages serves g heads.  Wave w owns rows 32w..32w+31.
 //   Keys stream in 64-key tiles (four 16-token pages) through two LDS
-//   buffers: while the waves compute on one, the next tile's K and V rows
-//   are in flight from the paged pools into registers and then written to
-//   the other buffer (K row-major; V transposed to [d][key] with a 4-key x
-//   8-element register transpose so LDS writes are 8 bytes wide).
+//   buffers, K and V both row-major as bf16 with each row's 16-byte chunks
+//   XOR-swizzled by the row index (conflict-free reads of a column of rows).
+//   bf16 pages are copied global -> LDS by buffer loads that write LDS
+//   directly (no registers in flight); the buffer descriptor of each page
+//   covers only the rows below ctx_len, so rows past the context arrive as
+//   zeros.  fp8 pages are loaded into registers, converted to bf16 exactly
+//   and written to the same layout.
 //   Per wave and tile, on v_mfma_f32_32x32x16_bf16:
-//     S^T[key][row] = K . Q^T      Q^T lives in registers for the whole call
-//     online softmax               each lane owns one row: its 32 scores of
-//                                  the tile sit in the lane (plus its pair
-//                                  lane 32 away), so max/sum need one swap
-//     O^T[d][row]  += V^T . P^T    P^T is the S^T accumulator re-packed in
-//                                  place; O^T's row is again the lane's row,
-//                                  so rescaling and the final 1/l stay local
-//   fp8 pages are converted to bf16 exactly on the way into LDS; the K scale
-//   multiplies the scores and the V scale is folded into P, per page.
+//     S^T[key][row] = K . Q^T      K rows by ds_read_b128, Q^T in registers
+//     online softmax               each lane owns one row (and shares it
+//                                  with the lane 32 away), so max and sum
+//                                  need one cross-lane swap
+//     O^T[d][row]  += V^T . P^T    V^T by ds_read_b64_tr_b16 (a 4-key x
+//                                  16-column block per 16 lanes, transposed
+//                                  in the read); P^T is the S^T accumulator
+//                                  re-packed in place; O^T's row is again
+//                                  the lane's row
 //   Workgroups of one kv head are placed on the same XCDs (blockIdx mod 8
 //   picks the XCD) so the K/V tiles they stream share that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -38,9 +41,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+#define LDS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKT = 64;  // keys per tile
+constexpr int kRsrcFlags = 0x00020000;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -62,103 +69,137 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Physical 16-byte chunk of logical chunk c in LDS row r.  Rows r..r+7 send
+// one logical chunk to 8 different bank groups; rows 4a..4a+3 send chunks
+// {c, c+1} (c even) to 8 different bank groups.
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
 template <int D, bool FP8>
 struct PGeo {
     static constexpr int EB = FP8 ? 1 : 2;
-    static constexpr int ROWB = D * EB;        // bytes of one token row in the pool
-    static constexpr int CPR = ROWB / 16;      // 16-byte chunks per pool row
-    static constexpr int EPC = 16 / EB;        // elements per chunk
-    static constexpr int KCH = kKT * CPR / 256;  // K chunks per thread per tile
-    static constexpr int VUN = 16 * CPR;       // V units (4 keys x 1 chunk) per tile
-    static constexpr int VUT = (VUN + 255) / 256;  // V units per thread (last may idle)
-    static constexpr int KS = D * 2 + 16;      // LDS K row stride (bytes)
-    static constexpr int VS = kKT * 2 + 8;     // LDS V^T row stride (bytes)
-    static constexpr int KBYTES = kKT * KS;
-    static constexpr int VBYTES = D * VS;
-    static constexpr int SBYTES = 64;          // per-page scales of the tile (fp8)
-    static constexpr int BUF = KBYTES + VBYTES + SBYTES;
-    static constexpr int DSTEPS = D / 16;      // k-steps of QK^T
-    static constexpr int DBLK = D / 32;        // 32-wide d blocks of O^T
-};
-
-template <int D, bool FP8>
-struct Stage {  // one thread's share of a tile in flight
-    u32x4 k[PGeo<D, FP8>::KCH];
-    u32x4 v[PGeo<D, FP8>::VUT][4];
-    float ks, vs;  // threads 0..3: scales of page tid of the tile
+    static constexpr int ROWB = D * EB;          // bytes of one token row in the pool
+    static constexpr int ROWL = D * 2;           // bytes of one row in LDS (bf16)
+    static constexpr int CPRL = ROWL / 16;       // 16-byte chunks per LDS row
+    static constexpr int TILEB = kKT * ROWL;     // one K (or V) tile in LDS
+    static constexpr int BUF = 2 * TILEB + 64;   // K, V, per-page scales
+    static constexpr int DSTEPS = D / 16;        // k-steps of QK^T
+    static constexpr int DBLK = D / 32;          // 32-wide d blocks of O^T
+    // direct (bf16) loads: 1 KiB LDS blocks
+    static constexpr int RPB = 1024 / ROWL;      // rows per block
+    static constexpr int NBW = (kKT / RPB) / 4;  // blocks per wave per tensor
+    // staged (fp8) loads: 16-byte pool chunks per thread per tensor
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int SCH = kKT * CPR / 256;
 };
 
 struct Blk {
-    int C, n_rows, base_pos, kh, Hk;
+    int C, kh, Hk;
     int64_t n_pages;
     const int32_t* bt;
 };
 
-// Page id of key `key` (or -1 when the key is at or past the context).
-__device__ __forceinline__ int page_of(const Blk& b, int key, int* bad)
+// Page of the q-th 16-key group of the tile at tile0 and the number of its
+// rows below the context; page -1 (and 0 rows) past the context or for an
+// entry outside the pool (which also raises *bad).
+__device__ __forceinline__ void tile_pages(const Blk& b, int tile0, int (&pg)[4], int (&rows)[4],
+                                           int* bad)
 {
-    if (key >= b.C)
-        return -1;
-    const int p = b.bt[key >> 4];
-    if (p < 0 || (int64_t)p >= b.n_pages) {
-        *bad = 1;
-        return -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int key0 = tile0 + 16 * q;
+        pg[q] = -1;
+        rows[q] = 0;
+        if (key0 < b.C) {
+            const int p = __builtin_amdgcn_readfirstlane(b.bt[key0 >> 4]);
+            if (p < 0 || (int64_t)p >= b.n_pages) {
+                *bad = 1;
+            } else {
+                pg[q] = p;
+                rows[q] = min(16, b.C - key0);
+            }
+        }
     }
-    return p;
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void stage_load(Stage<D, FP8>& st, const Blk& b, const uint8_t* kp,
+// bf16: every wave issues its share of the tile's 1 KiB blocks as buffer
+// loads that write LDS directly.
+template <int D>
+__device__ __forceinline__ void issue_direct(char* kbuf, char* vbuf, const Blk& b,
+                                             const uint8_t* kp, const uint8_t* vp, int tile0,
+                                             int wave, const int (&loff)[PGeo<D, false>::NBW],
+                                             int* bad)
+{
+    using G = PGeo<D, false>;
+    int pg[4], rows[4];
+    tile_pages(b, tile0, pg, rows, bad);
+#pragma unroll
+    for (int i = 0; i < G::NBW; ++i) {
+        const int blk = wave * G::NBW + i;
+        const int q = (blk * G::RPB) >> 4;
+        const int voff = loff[i];
+        const int64_t base = ((int64_t)(pg[q] < 0 ? 0 : pg[q]) * b.Hk + b.kh) * 16 * G::ROWB;
+        const int nrec = rows[q] * G::ROWB;
+        __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kp + base), (short)0, nrec, kRsrcFlags);
+        __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vp + base), (short)0, nrec, kRsrcFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(kbuf + blk * 1024), 16, voff, 0,
+                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(vbuf + blk * 1024), 16, voff, 0,
+                                                 0, 0);
+    }
+}
+
+// fp8: a thread's share of the tile in registers between load and store.
+template <int D>
+struct Staged {
+    u32x4 k[PGeo<D, true>::SCH];
+    u32x4 v[PGeo<D, true>::SCH];
+    float ks, vs;
+};
+
+template <int D>
+__device__ __forceinline__ void stage_load(Staged<D>& st, const Blk& b, const uint8_t* kp,
                                            const uint8_t* vp, const float* ksc, const float* vsc,
                                            int tile0, int tid, int* bad)
 {
-    using G = PGeo<D, FP8>;
+    using G = PGeo<D, true>;
+    int pg[4], rows[4];
+    tile_pages(b, tile0, pg, rows, bad);
 #pragma unroll
-    for (int i = 0; i < G::KCH; ++i) {
+    for (int i = 0; i < G::SCH; ++i) {
         const int c = i * 256 + tid;
         const int key = c / G::CPR, piece = c % G::CPR;
-        const int pg = page_of(b, tile0 + key, bad);
-        if (pg >= 0)
-            st.k[i] = *(const u32x4*)(kp + (((int64_t)pg * b.Hk + b.kh) * 16 + ((tile0 + key) & 15)) *
-                                               G::ROWB + piece * 16);
-        else
+        const int q = key >> 4;
+        if ((key & 15) < rows[q]) {
+            const int64_t off =
+                (((int64_t)pg[q] * b.Hk + b.kh) * 16 + (key & 15)) * G::ROWB + piece * 16;
+            st.k[i] = *(const u32x4*)(kp + off);
+            st.v[i] = *(const u32x4*)(vp + off);
+        } else {
             st.k[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < G::VUT; ++i) {
-        const int u = i * 256 + tid;
-        const int kg = u & 15, piece = u >> 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = tile0 + 4 * kg + j;
-            const int pg = u < G::VUN ? page_of(b, key, bad) : -1;
-            if (pg >= 0)
-                st.v[i][j] = *(const u32x4*)(vp + (((int64_t)pg * b.Hk + b.kh) * 16 + (key & 15)) *
-                                                      G::ROWB + piece * 16);
-            else
-                st.v[i][j] = u32x4{0u, 0u, 0u, 0u};
+            st.v[i] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    if (FP8 && tid < 4) {
-        const int pg = page_of(b, tile0 + 16 * tid, bad);
-        st.ks = pg >= 0 ? ksc[(int64_t)pg * b.Hk + b.kh] : 0.f;
-        st.vs = pg >= 0 ? vsc[(int64_t)pg * b.Hk + b.kh] : 0.f;
+    if (tid < 4) {  // pages past the context: scale 1 (their keys are masked)
+        st.ks = pg[tid] >= 0 ? ksc[(int64_t)pg[tid] * b.Hk + b.kh] : 1.f;
+        st.vs = pg[tid] >= 0 ? vsc[(int64_t)pg[tid] * b.Hk + b.kh] : 1.f;
     }
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, char* buf, int tid)
+template <int D>
+__device__ __forceinline__ void stage_store(const Staged<D>& st, char* kbuf, char* vbuf,
+                                            float* sc, int tid)
 {
-    using G = PGeo<D, FP8>;
-    char* ks = buf;
-    char* vt = buf + G::KBYTES;
-    float* sc = (float*)(buf + G::KBYTES + G::VBYTES);
+    using G = PGeo<D, true>;
 #pragma unroll
-    for (int i = 0; i < G::KCH; ++i) {
+    for (int i = 0; i < G::SCH; ++i) {
         const int c = i * 256 + tid;
         const int key = c / G::CPR, piece = c % G::CPR;
-        if constexpr (FP8) {
-            const u32x4 w = st.k[i];
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+            const u32x4 w = kv ? st.v[i] : st.k[i];
+            char* row = (kv ? vbuf : kbuf) + key * G::ROWL;
             u32x4 lo, hi;
             lo[0] = fp8x2_to_bf16x2<false>(w[0]);
             lo[1] = fp8x2_to_bf16x2<true>(w[0]);
@@ -168,45 +209,11 @@ __device__ __forceinline__ void stage_store(const Stage<D, FP8>& st, char* buf, 
             hi[1] = fp8x2_to_bf16x2<true>(w[2]);
             hi[2] = fp8x2_to_bf16x2<false>(w[3]);
             hi[3] = fp8x2_to_bf16x2<true>(w[3]);
-            *(u32x4*)(ks + key * G::KS + piece * 32) = lo;
-            *(u32x4*)(ks + key * G::KS + piece * 32 + 16) = hi;
-        } else {
-            *(u32x4*)(ks + key * G::KS + piece * 16) = st.k[i];
+            *(u32x4*)(row + ((2 * piece) ^ swz(key)) * 16) = lo;
+            *(u32x4*)(row + ((2 * piece + 1) ^ swz(key)) * 16) = hi;
         }
     }
-#pragma unroll
-    for (int i = 0; i < G::VUT; ++i) {
-        const int u = i * 256 + tid;
-        if (u >= G::VUN)
-            continue;
-        const int kg = u & 15, piece = u >> 4;
-        // bf16 elements of the 4 keys: dword w of key j holds elements 2w, 2w+1
-        uint32_t e[4][G::EPC / 2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (FP8) {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    e[j][2 * w] = fp8x2_to_bf16x2<false>(st.v[i][j][w]);
-                    e[j][2 * w + 1] = fp8x2_to_bf16x2<true>(st.v[i][j][w]);
-                }
-            } else {
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    e[j][w] = st.v[i][j][w];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < G::EPC; ++x) {
-            const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
-            u32x2 o;
-            o[0] = __builtin_amdgcn_perm(e[1][x >> 1], e[0][x >> 1], sel);
-            o[1] = __builtin_amdgcn_perm(e[3][x >> 1], e[2][x >> 1], sel);
-            const int d = piece * G::EPC + x;
-            *(u32x2*)(vt + d * G::VS + kg * 8) = o;
-        }
-    }
-    if (FP8 && tid < 4) {
+    if (tid < 4) {
         sc[tid] = st.ks;
         sc[4 + tid] = st.vs;
     }
@@ -216,7 +223,7 @@ template <int D, bool FP8>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
 {
     using G = PGeo<D, FP8>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * G::BUF];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * G::BUF];
     __shared__ int s_bad;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,12 +242,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
 
     Blk b;
     b.C = a.ctx_len;
-    b.n_rows = a.n_rows;
-    b.base_pos = a.ctx_len - a.n_rows;
     b.kh = kh;
     b.Hk = Hk;
     b.n_pages = a.n_pages;
     b.bt = a.block_table;
+    const int base_pos = a.ctx_len - a.n_rows;
 
     // This lane's query row.
     const int wrow = 32 * wave + l32;          // 0..127 in the workgroup
@@ -248,10 +254,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
     const int r = pb * BP + p;                 // row of the call
     const bool valid = r < a.n_rows;
     const int h = kh * g + hg;
-    const int pos = valid ? b.base_pos + r : -1;
+    const int pos = valid ? base_pos + r : -1;
     const int rlast = min(a.n_rows, (pb + 1) * BP) - 1;
-    const int maxpos = b.base_pos + rlast;     // last key any row here needs
-    const int minpos = b.base_pos + pb * BP;
+    const int maxpos = base_pos + rlast;       // last key any row here needs
+    const int minpos = base_pos + pb * BP;
     const int nt = (maxpos + kKT) / kKT;
 
     // Q^T operand: 8 bf16 of row `wrow` per k-step (d = 16 st + 8 kb + i).
@@ -278,76 +284,142 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
     const uint8_t* kp = (const uint8_t*)a.k_pool;
     const uint8_t* vp = (const uint8_t*)a.v_pool;
 
-    Stage<D, FP8> st;
-    stage_load<D, FP8>(st, b, kp, vp, a.k_scale, a.v_scale, 0, tid, &bad);
-    stage_store<D, FP8>(st, smem, tid);
+    // Per-lane byte offsets, fixed for the whole call.
+    // Direct loads: instruction i of this wave fills LDS block wave*NBW + i;
+    // this lane writes row rr, physical chunk pc of it and so fetches
+    // logical chunk pc ^ swz(row) of that row.
+    int loff[G::NBW];
+    if constexpr (!FP8) {
+        const int rr = lane / G::CPRL, pc = lane % G::CPRL;
+#pragma unroll
+        for (int i = 0; i < G::NBW; ++i) {
+            const int row = (wave * G::NBW + i) * G::RPB + rr;
+            loff[i] = (row & 15) * G::ROWB + ((pc ^ swz(row)) * 16);
+        }
+    }
+    // K reads: row 32 kblk + l32, logical chunk 2 s2 + kb.  The swizzle only
+    // touches the low 3 chunk bits, so step s2 = base(s2 % 4) + 128 (s2 / 4).
+    int koff[2][4];
+#pragma unroll
+    for (int kblk = 0; kblk < 2; ++kblk) {
+        const int kr = 32 * kblk + l32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            koff[kblk][j] = kr * G::ROWL + 16 * ((2 * j + kb) ^ swz(kr));
+    }
+    // V reads (ds_read_b64_tr_b16): the 16-lane group (kb, half) reads keys
+    // 16 s4 + 8 h + 4 kb + s/4 (s = lane in group), columns
+    // 32 db + 16 half + 4 (s % 4) .. +3.  swz() of those keys does not depend
+    // on s4 or h, so a read = base(db % 2) + s4 * 16 rows + h * 8 rows +
+    // 128 (db / 2).
+    int voff[2];
+    {
+        const int grp = lane >> 4, s16 = lane & 15;
+        const int vkey = 4 * kb + (s16 >> 2);
+        const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);
+        const int sw = swz(vkey);
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            voff[par] = vkey * G::ROWL + 16 * ((4 * par + (vcol >> 3)) ^ sw) + (vcol & 7) * 2;
+    }
+
+    Staged<D> stg;
+    char* buf0 = smem;
+    if constexpr (FP8) {
+        stage_load<D>(stg, b, kp, vp, a.k_scale, a.v_scale, 0, tid, &bad);
+        stage_store<D>(stg, buf0, buf0 + G::TILEB, (float*)(buf0 + 2 * G::TILEB), tid);
+    } else {
+        issue_direct<D>(buf0, buf0 + G::TILEB, b, kp, vp, 0, wave, loff, &bad);
+        __builtin_amdgcn_s_waitcnt(0);
+    }
     __syncthreads();
 
+    // Lazy rescaling: the reference max m only moves when a score exceeds it
+    // by more than 2^kTau, so P stays <= 2^kTau and O/l are rescaled rarely.
+    constexpr float kTau = 8.f;
     for (int t = 0; t < nt; ++t) {
         const int tile0 = t * kKT;
-        if (t + 1 < nt)
-            stage_load<D, FP8>(st, b, kp, vp, a.k_scale, a.v_scale, tile0 + kKT, tid, &bad);
+        char* nbuf = smem + ((t + 1) & 1) * G::BUF;
+        if (t + 1 < nt) {
+            if constexpr (FP8)
+                stage_load<D>(stg, b, kp, vp, a.k_scale, a.v_scale, tile0 + kKT, tid, &bad);
+            else
+                issue_direct<D>(nbuf, nbuf + G::TILEB, b, kp, vp, tile0 + kKT, wave, loff, &bad);
+        }
         const char* buf = smem + (t & 1) * G::BUF;
         const char* ks = buf;
-        const char* vt = buf + G::KBYTES;
-        const float* sc = (const float*)(buf + G::KBYTES + G::VBYTES);
+        const char* vs = buf + G::TILEB;
+        const float* sc = (const float*)(buf + 2 * G::TILEB);
 
-        // S^T for the two 32-key blocks of the tile.
+        // S^T for the two 32-key blocks of the tile (two independent chains).
         f32x16 acc[2];
 #pragma unroll
-        for (int kblk = 0; kblk < 2; ++kblk) {
+        for (int kblk = 0; kblk < 2; ++kblk)
 #pragma unroll
             for (int x = 0; x < 16; ++x)
                 acc[kblk][x] = 0.f;
-            const char* krow = ks + (32 * kblk + l32) * G::KS + 16 * kb;
 #pragma unroll
-            for (int s2 = 0; s2 < G::DSTEPS; ++s2) {
-                const u32x4 kw = *(const u32x4*)(krow + 32 * s2);
+        for (int s2 = 0; s2 < G::DSTEPS; ++s2) {
+#pragma unroll
+            for (int kblk = 0; kblk < 2; ++kblk) {
+                const u32x4 kw = *(const u32x4*)(ks + koff[kblk][s2 & 3] + 128 * (s2 >> 2));
                 acc[kblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, kw), __builtin_bit_cast(bf16x8, qop[s2]), acc[kblk],
                     0, 0, 0);
             }
         }
 
-        // Scores, mask, online softmax (row = this lane's row).
-        const bool diag = tile0 + kKT - 1 > minpos;
+        // Scores in log2 units; the causal edge only crosses the last tiles.
+        if (tile0 + kKT - 1 > minpos) {
+#pragma unroll
+            for (int kblk = 0; kblk < 2; ++kblk)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int key = tile0 + 32 * kblk + 8 * (x >> 2) + 4 * kb + (x & 3);
+                    if (key > pos)
+                        acc[kblk][x] = neg_inf();
+                }
+        }
         float tmax = neg_inf();
 #pragma unroll
         for (int kblk = 0; kblk < 2; ++kblk) {
-            float s0 = sm_log2, s1 = sm_log2;
-            if constexpr (FP8) {
-                s0 = sc[2 * kblk] * sm_log2;
-                s1 = sc[2 * kblk + 1] * sm_log2;
-            }
+            const float s0 = FP8 ? sc[2 * kblk] * sm_log2 : sm_log2;
+            const float s1 = FP8 ? sc[2 * kblk + 1] * sm_log2 : sm_log2;
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
-                const int key = tile0 + 32 * kblk + 8 * (x >> 2) + 4 * kb + (x & 3);
-                float v = acc[kblk][x] * ((x >> 3) ? s1 : s0);
-                if (diag)
-                    v = key <= pos ? v : neg_inf();
-                acc[kblk][x] = v;
-                tmax = fmaxf(tmax, v);
+                acc[kblk][x] = acc[kblk][x] * ((x >> 3) ? s1 : s0);
+                tmax = fmaxf(tmax, acc[kblk][x]);
             }
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(m, tmax);
-        const float muse = mnew == neg_inf() ? 0.f : mnew;
-        const float alpha = m == muse ? 1.f : __builtin_amdgcn_exp2f(m - muse);
+        if (__builtin_amdgcn_ballot_w64(tmax > m + kTau)) {
+            const float mnew = fmaxf(m, tmax);
+            const float alpha =
+                m == neg_inf() ? 0.f : (m == mnew ? 1.f : __builtin_amdgcn_exp2f(m - mnew));
+            l = l * alpha;
+#pragma unroll
+            for (int db = 0; db < G::DBLK; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; ++x)
+                    O[db][x] = O[db][x] * alpha;
+            m = mnew;
+        }
+        const float muse = m == neg_inf() ? 0.f : m;
         float psum = 0.f;
         u32x4 pb4[4];  // P^T operands of the 4 PV k-steps
 #pragma unroll
         for (int kblk = 0; kblk < 2; ++kblk) {
-            float vsc0 = 1.f, vsc1 = 1.f;
+            float v0 = 1.f, v1 = 1.f;
             if constexpr (FP8) {
-                vsc0 = sc[4 + 2 * kblk];
-                vsc1 = sc[4 + 2 * kblk + 1];
+                v0 = sc[4 + 2 * kblk];
+                v1 = sc[4 + 2 * kblk + 1];
             }
             float pv[16];
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
                 const float e = __builtin_amdgcn_exp2f(acc[kblk][x] - muse);
                 psum = psum + e;
-                pv[x] = FP8 ? e * ((x >> 3) ? vsc1 : vsc0) : e;
+                pv[x] = FP8 ? e * ((x >> 3) ? v1 : v0) : e;
             }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
@@ -355,34 +427,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
                 for (int w = 0; w < 4; ++w)
                     pb4[2 * kblk + h2][w] = pack_bf16(pv[8 * h2 + 2 * w], pv[8 * h2 + 2 * w + 1]);
         }
-        psum = psum + __shfl_xor(psum, 32, 64);
-        l = l * alpha + psum;
-        m = mnew;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-            for (int db = 0; db < G::DBLK; ++db)
-#pragma unroll
-                for (int x = 0; x < 16; ++x)
-                    O[db][x] = O[db][x] * alpha;
-        }
+        l = l + (psum + __shfl_xor(psum, 32, 64));
 
         // O^T += V^T . P^T over the tile's 4 16-key steps.
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
             for (int db = 0; db < G::DBLK; ++db) {
-                const char* vrow = vt + (32 * db + l32) * G::VS + (16 * s4 + 4 * kb) * 2;
-                const u32x2 lo = *(const u32x2*)vrow;
-                const u32x2 hi = *(const u32x2*)(vrow + 16);
-                const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                const char* v0 = vs + voff[db & 1] + s4 * 16 * G::ROWL + 128 * (db >> 1);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)v0);
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(v0 + 8 * G::ROWL));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 va = u32x4{l2[0], l2[1], h2[0], h2[1]};
                 O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb4[s4]), O[db], 0,
                     0, 0);
             }
         }
 
-        if (t + 1 < nt)
-            stage_store<D, FP8>(st, smem + ((t + 1) & 1) * G::BUF, tid);
+        if (t + 1 < nt) {
+            if constexpr (FP8)
+                stage_store<D>(stg, nbuf, nbuf + G::TILEB, (float*)(nbuf + 2 * G::TILEB), tid);
+            else
+                __builtin_amdgcn_s_waitcnt(0);
+        }
         __syncthreads();
     }
 
