@@ -95,6 +95,10 @@ int check_common(const char* fn, const void* q, const void* k_pool, const void* 
         return fail(ATTN_E_UNSUPPORTED, "%s: head_dim %d not served (128, 256)", fn, head_dim);
     if (page_size != ATTN_PAGE_SIZE)
         return fail(ATTN_E_UNSUPPORTED, "%s: page_size %d not served (16)", fn, page_size);
+    // The kernels address the per-page scale arrays through one bounds-checked
+    // buffer resource each, which spans less than 2 GiB.
+    if (n_pages * (int64_t)n_head_kv * 4 >= ((int64_t)1 << 31))
+        return fail(ATTN_E_UNSUPPORTED, "%s: n_pages * n_head_kv above 2^29", fn);
     return ATTN_OK;
 }
 
@@ -146,6 +150,10 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
         return fail(ATTN_E_UNSUPPORTED,
                     "%s: %d rows x %d heads per kv head at head_dim %d not served", fn, rows, g,
                     head_dim);
+    // One sequence's query rows, and one split's partial outputs, are each
+    // addressed through a buffer resource spanning less than 2 GiB.
+    if ((int64_t)rows * n_head * head_dim * 4 >= ((int64_t)1 << 31))
+        return fail(ATTN_E_UNSUPPORTED, "%s: rows * n_head * head_dim too large", fn);
     const size_t need = split_ws_bytes(rows, n_seq, max_pages, n_head, head_dim);
     rc = check_workspace(fn, workspace, workspace_bytes, need);
     if (rc != ATTN_OK)

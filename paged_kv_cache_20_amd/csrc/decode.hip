@@ -11,30 +11,45 @@
 //   so the items a row takes part in, and everything computed inside them,
 //   depend on the row's position and its sequence's own data only.  Each wave
 //   of a persistent grid walks items (wave, wave + total waves, ...); which
-//   wave takes an item changes nothing in its arithmetic.
+//   wave takes an item changes nothing in its arithmetic.  The block-table
+//   entries of a wave's next item are fetched while it works on the current
+//   one.
+//
+// Streaming
+//   Keys stream in tiles of KT (16 or 32, fixed per head_dim and KV dtype)
+//   through a ring of NBUF register buffers: the loads of tile i + NBUF - 1
+//   are issued before tile i is computed, so NBUF - 1 tiles are in flight
+//   while one is consumed.  Every load is a bounds-checked buffer load whose
+//   resource covers only the rows of its (page, kv head) chunk below the end
+//   of the item: rows past the context, and whole pages past the item, read
+//   as zeros without touching memory.  No load sits under a branch, so the
+//   compiler's counter waits release each tile as soon as its own loads are
+//   done.  Page ids and fp8 scales are wave-uniform (scalar registers).
 //
 // Inside an item (one 64-lane wave)
 //   Query rows are packed into 16-slot MFMA tiles.  A tile holds floor(16/g)
 //   positions x g heads of the kv group (g = n_head / n_head_kv); position p
 //   and head-in-group c sit in slot g * (p mod floor(16/g)) + c, so a
 //   position occupies the same MFMA column in a decode call and in a verify
-//   call.  Keys stream in tiles of 32 (two 16-token pages):
+//   call.  Per key tile:
 //     S^T[key][slot] = K . Q^T     v_mfma_f32_16x16x32_bf16, keys as rows
 //     online softmax per slot      exp2, max/sum across the wave's 4 k-groups
-//     O[slot][d]    += P . V       v_mfma_f32_16x16x32_bf16
+//     O[slot][d]    += P . V       v_mfma_f32_16x16x32_bf16 (32-key tiles) or
+//                                  v_mfma_f32_16x16x16_bf16 (16-key tiles)
 //   The S^T accumulator layout (lane = slot + 16 * key group) is exactly the
 //   A-operand layout P needs, so P never moves between lanes.  K is read in
 //   A-operand order (16-byte pieces, one key row per lane); V is read
 //   row-contiguous (each 16 lanes cover whole token rows) and transposed in
 //   registers with byte permutes.  fp8 codes become bf16 exactly in
 //   registers; the K scale multiplies the scores, the V scale is folded into
-//   P, both per page.
-//   Keys at or beyond ctx_len are never loaded (zeros take their place) and
-//   are masked; a fully masked tile leaves m, l and O bit-identical.
+//   P, both per page.  Keys past a row's position are masked; a fully masked
+//   tile leaves m, l and O bit-identical.
 //
 // Combine: per (sequence, row, head), splits 0 .. floor(pos / 512) are merged
-// in increasing order: M = max m_j, w_j = exp2(m_j - M),
-// out = sum w_j o_j / sum w_j l_j, rounded to bf16.
+// in a fixed order that depends on their count only: M = max m_j,
+// w_j = exp2(m_j - M), den = sum w_j l_j (a fixed butterfly inside each group
+// of 64 splits, groups in increasing order), num = sum w_j o_j (j
+// increasing), out = num / den rounded to bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,13 +60,20 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;  // waves per block
-constexpr int kKT = 32;    // keys per inner tile
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle;
+// accesses at or past num_records return zero.
+constexpr int kRsrcFlags = 0x00020000;
+// A buffer offset past every resource the kernels build (each covers less
+// than 2 GiB), with room for the instruction offsets added to it.
+constexpr uint32_t kFar = 0x80000000u;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -74,25 +96,57 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ int rdlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float rdlane_f(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcFlags);
+}
 
 template <int D, bool FP8>
 struct Geo {
     static constexpr int EB = FP8 ? 1 : 2;      // bytes per stored element
     static constexpr int ROWB = D * EB;         // bytes per token row of one kv head
+    static constexpr int CHUNKB = 16 * ROWB;    // bytes of one (page, kv head) chunk
     static constexpr int STEPS = D / 32;        // k-steps of the QK^T contraction
-    static constexpr int KLD = ROWB / 64;       // 16-byte K loads per lane per key block
+    static constexpr int KLD = ROWB / 64;       // 16-byte K loads per lane per 16-key block
     static constexpr int VPB = ROWB / 16;       // V bytes per lane per token
     static constexpr int VDW = VPB / 4;         // ... in dwords
     static constexpr int DB = D / 16;           // output columns per lane (d blocks)
-    static constexpr int RAW = 2 * KLD * 4 + 8 * VDW;  // raw tile dwords per lane
+    // Keys per tile: 32, except bf16 at head_dim 256 (16, one page), which
+    // keeps a tile at 16 KiB.  A property of (head_dim, dtype) only, so a
+    // row's arithmetic never depends on how many rows the call has.
+    static constexpr int KT = (!FP8 && D == 256) ? 16 : 32;
+    static constexpr int KB = KT / 16;          // 16-key blocks per tile
+    static constexpr int KEYS = 4 * KB;         // keys a lane feeds to the PV product
 };
 
 template <int D, bool FP8>
 struct Raw {
-    u32x4 k[2][Geo<D, FP8>::KLD];
-    uint32_t v[8][Geo<D, FP8>::VDW];
+    u32x4 k[Geo<D, FP8>::KB][Geo<D, FP8>::KLD];
+    uint32_t v[Geo<D, FP8>::KEYS][Geo<D, FP8>::VDW];
+};
+
+// Register plan of an instantiation: waves per SIMD it is compiled for
+// (two where two tiles, Q and O fit in half the register file) and the depth
+// of its tile ring (three tiles where they fit beside Q and O).  With one
+// wave per SIMD the O accumulators live in the AGPR half of the file.
+template <int D, bool FP8, int NT>
+struct Plan {
+    using G = Geo<D, FP8>;
+    static constexpr int RAW = G::KB * G::KLD * 4 + G::KEYS * G::VDW;  // dwords per tile
+    static constexpr int QOP = NT * G::STEPS * 4;
+    static constexpr int OREG = NT * G::DB * 4;
+    static constexpr int OCC = (2 * RAW + QOP + OREG <= 176) ? 2 : 1;
+    static constexpr int NBUF = OCC == 2 ? ((3 * RAW + QOP + OREG <= 160) ? 3 : 2)
+                                         : ((3 * RAW + QOP <= 224) ? 3 : 2);
 };
 
 // Element offset (in the query row) of the first of the 8 d-values that
@@ -124,57 +178,50 @@ __device__ __forceinline__ bf16x8 k_operand(const u32x4* kr, int st)
     }
 }
 
-// Key (within the 32-key tile) that lane group kb feeds at k-slot i of the
-// PV product; the same keys the lane holds in its S^T accumulators.
-__device__ __forceinline__ int pv_key(int kb, int i) { return i < 4 ? 4 * kb + i : 12 + 4 * kb + i; }
-
+// Loads of one key tile.  pg0/pg1: pages of its two 16-key blocks (pg1 is
+// unused for 16-key tiles); n0/n1: rows of each page inside the item (0..16).
+// koff: this lane's byte offset of its K row piece, voff: of its first V row
+// piece, inside a chunk.  Key kk = 4 kb + i (i < 4) or 16 + 4 kb + (i - 4)
+// of the tile feeds PV k-slot i of lane group kb; those are the keys the
+// lane's S^T accumulators hold.
 template <int D, bool FP8>
-__device__ __forceinline__ void load_tile(Raw<D, FP8>& t, const uint8_t* __restrict__ kp,
-                                          const uint8_t* __restrict__ vp, int pg0, int pg1,
-                                          int kt, int C, int Hk, int kh, int n, int kb)
+__device__ __forceinline__ void load_tile(Raw<D, FP8>& t, const uint8_t* kp, const uint8_t* vp,
+                                          int64_t chunk0, int64_t chunk1, int n0, int n1,
+                                          uint32_t koff, uint32_t voff)
 {
     using G = Geo<D, FP8>;
 #pragma unroll
-    for (int kblk = 0; kblk < 2; ++kblk) {
-        const int key = kt + 16 * kblk + n;
-        const int pg = kblk ? pg1 : pg0;
-        if (key < C) {
-            const uint8_t* row = kp + (((int64_t)pg * Hk + kh) * 16 + n) * G::ROWB + 16 * kb;
+    for (int kblk = 0; kblk < G::KB; ++kblk) {
+        const int64_t ch = kblk ? chunk1 : chunk0;
+        const int nr = kblk ? n1 : n0;
+        const __amdgpu_buffer_rsrc_t rk = rsrc(kp + ch * G::CHUNKB, (uint32_t)(nr * G::ROWB));
 #pragma unroll
-            for (int c = 0; c < G::KLD; ++c)
-                t.k[kblk][c] = *(const u32x4*)(row + 64 * c);
-        } else {
-#pragma unroll
-            for (int c = 0; c < G::KLD; ++c)
-                t.k[kblk][c] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int c = 0; c < G::KLD; ++c)
+            t.k[kblk][c] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * c, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int kk = pv_key(kb, i);
-        const int key = kt + kk;
-        const int pg = (kk >> 4) ? pg1 : pg0;
-        if (key < C) {
-            const uint8_t* row =
-                vp + (((int64_t)pg * Hk + kh) * 16 + (kk & 15)) * G::ROWB + n * G::VPB;
+    for (int kblk = 0; kblk < G::KB; ++kblk) {
+        const int64_t ch = kblk ? chunk1 : chunk0;
+        const int nr = kblk ? n1 : n0;
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vp + ch * G::CHUNKB, (uint32_t)(nr * G::ROWB));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = voff + i * G::ROWB;
+            uint32_t* dst = t.v[4 * kblk + i];
             if constexpr (G::VDW == 2) {
-                const u32x2 w = *(const u32x2*)row;
-                t.v[i][0] = w[0];
-                t.v[i][1] = w[1];
+                const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+                dst[0] = w[0];
+                dst[1] = w[1];
             } else {
 #pragma unroll
                 for (int c = 0; c < G::VDW / 4; ++c) {
-                    const u32x4 w = *(const u32x4*)(row + 16 * c);
-                    t.v[i][4 * c + 0] = w[0];
-                    t.v[i][4 * c + 1] = w[1];
-                    t.v[i][4 * c + 2] = w[2];
-                    t.v[i][4 * c + 3] = w[3];
+                    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rv, off + 16 * c, 0, 0);
+                    dst[4 * c + 0] = w[0];
+                    dst[4 * c + 1] = w[1];
+                    dst[4 * c + 2] = w[2];
+                    dst[4 * c + 3] = w[3];
                 }
             }
-        } else {
-#pragma unroll
-            for (int c = 0; c < G::VDW; ++c)
-                t.v[i][c] = 0u;
         }
     }
 }
@@ -194,19 +241,20 @@ template <int D, bool FP8, int NT>
 __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (&qop)[NT][D / 32],
                                              const int (&last)[NT], float (&m)[NT], float (&l)[NT],
                                              f32x4 (&O)[NT][D / 16], int kt, float sc0, float sc1,
-                                             float vs0, float vs1, int lane, int kb)
+                                             float vs0, float vs1, int kb)
 {
     using G = Geo<D, FP8>;
-    f32x4 acc[2][NT];
+    constexpr int KB = G::KB;
+    f32x4 acc[KB][NT];
 #pragma unroll
-    for (int kblk = 0; kblk < 2; ++kblk)
+    for (int kblk = 0; kblk < KB; ++kblk)
 #pragma unroll
         for (int tau = 0; tau < NT; ++tau)
             acc[kblk][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < G::STEPS; ++st) {
 #pragma unroll
-        for (int kblk = 0; kblk < 2; ++kblk) {
+        for (int kblk = 0; kblk < KB; ++kblk) {
             const bf16x8 ka = k_operand<D, FP8>(t.k[kblk], st);
 #pragma unroll
             for (int tau = 0; tau < NT; ++tau)
@@ -215,14 +263,14 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
         }
     }
 
-    u32x4 pa[NT];
+    uint32_t pa[NT][2 * KB];
     float alpha[NT];
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
-        float sv[2][4];
+        float sv[KB][4];
         float tmax = neg_inf();
 #pragma unroll
-        for (int kblk = 0; kblk < 2; ++kblk)
+        for (int kblk = 0; kblk < KB; ++kblk)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = kt + 16 * kblk + 4 * kb + r;
@@ -235,14 +283,15 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
         const float mnew = fmaxf(m[tau], tmax);
         const float muse = mnew == neg_inf() ? 0.f : mnew;
         const float al = m[tau] == muse ? 1.f : __builtin_amdgcn_exp2f(m[tau] - muse);
-        float p[2][4];
+        float p[KB][4];
 #pragma unroll
-        for (int kblk = 0; kblk < 2; ++kblk)
+        for (int kblk = 0; kblk < KB; ++kblk)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 p[kblk][r] = __builtin_amdgcn_exp2f(sv[kblk][r] - muse);
-        float psum = ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                     ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+        float psum = (p[0][0] + p[0][1]) + (p[0][2] + p[0][3]);
+        if constexpr (KB == 2)
+            psum = psum + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
         psum = psum + shfl_xor_f(psum, 16);
         psum = psum + shfl_xor_f(psum, 32);
         l[tau] = l[tau] * al + psum;
@@ -250,15 +299,16 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
         alpha[tau] = al;
         if constexpr (FP8) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[0][r] = p[0][r] * vs0;
-                p[1][r] = p[1][r] * vs1;
-            }
+            for (int kblk = 0; kblk < KB; ++kblk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p[kblk][r] = p[kblk][r] * (kblk ? vs1 : vs0);
         }
-        pa[tau][0] = pack_bf16(p[0][0], p[0][1]);
-        pa[tau][1] = pack_bf16(p[0][2], p[0][3]);
-        pa[tau][2] = pack_bf16(p[1][0], p[1][1]);
-        pa[tau][3] = pack_bf16(p[1][2], p[1][3]);
+#pragma unroll
+        for (int kblk = 0; kblk < KB; ++kblk) {
+            pa[tau][2 * kblk + 0] = pack_bf16(p[kblk][0], p[kblk][1]);
+            pa[tau][2 * kblk + 1] = pack_bf16(p[kblk][2], p[kblk][3]);
+        }
     }
 
     // Rescale O rows (slot 4*kb + r) by their slot's alpha; skipping a
@@ -279,10 +329,10 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
     }
 
     // V B-operands: column n of d-block jb is d = n * DB + jb; k-slot i is
-    // token pv_key(kb, i).
-    uint32_t vb[8][G::DB / 2];  // bf16 pieces: token i, dword w = elements 2w, 2w+1
+    // the key described at load_tile.
+    uint32_t vb[G::KEYS][G::DB / 2];  // bf16 pairs: dword w = elements 2w, 2w+1
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < G::KEYS; ++i) {
         if constexpr (FP8) {
 #pragma unroll
             for (int w = 0; w < G::VDW; ++w) {
@@ -298,27 +348,77 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
 #pragma unroll
     for (int jb = 0; jb < G::DB; ++jb) {
         const uint32_t sel = (jb & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 b;
+        uint32_t b[2 * KB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 2 * KB; ++u)
             b[u] = __builtin_amdgcn_perm(vb[2 * u + 1][jb >> 1], vb[2 * u][jb >> 1], sel);
 #pragma unroll
-        for (int tau = 0; tau < NT; ++tau)
-            O[tau][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, pa[tau]), __builtin_bit_cast(bf16x8, b), O[tau][jb], 0,
-                0, 0);
+        for (int tau = 0; tau < NT; ++tau) {
+            if constexpr (KB == 2) {
+                const u32x4 pv = {pa[tau][0], pa[tau][1], pa[tau][2], pa[tau][3]};
+                const u32x4 bv = {b[0], b[1], b[2], b[3]};
+                O[tau][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, pv), __builtin_bit_cast(bf16x8, bv), O[tau][jb], 0,
+                    0, 0);
+            } else {
+                const u32x2 pv = {pa[tau][0], pa[tau][1]};
+                const u32x2 bv = {b[0], b[1]};
+                O[tau][jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(s16x4, pv), __builtin_bit_cast(s16x4, bv), O[tau][jb], 0,
+                    0, 0);
+            }
+        }
     }
-    (void)lane;
 }
 
 __device__ __forceinline__ bool ctx_ok(int C, int R, int64_t cap) { return C >= R && (int64_t)C <= cap; }
 
+// A work item resolved to its sequence, split and kv head.
+struct Item {
+    int s, j, kh, C, t0, t1, npg;
+};
+
+__device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_len, int S, int Hk,
+                                             int item)
+{
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= item)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    Item it;
+    it.s = __builtin_amdgcn_readfirstlane(lo);
+    const int local = __builtin_amdgcn_readfirstlane(item - s_pre[it.s]);
+    it.j = local / Hk;
+    it.kh = local - it.j * Hk;
+    it.C = __builtin_amdgcn_readfirstlane(s_len[it.s]);
+    it.t0 = it.j * kChunk;
+    it.t1 = min(it.t0 + kChunk, it.C);
+    it.npg = (it.t1 - it.t0 + 15) >> 4;
+    return it;
+}
+
+// Lane e < npg receives block-table entry e of the item (0 elsewhere, and
+// everywhere if `live` is false).
+__device__ __forceinline__ int fetch_pages(const SplitArgs& a, const Item& it, bool live)
+{
+    const int32_t* row = a.block_table + (int64_t)it.s * a.max_pages + (it.t0 >> 4);
+    const __amdgpu_buffer_rsrc_t r = rsrc(row, live ? (uint32_t)it.npg * 4u : 0u);
+    const int lane = threadIdx.x & 63;
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4u, 0, 0);
+}
+
 template <int D, bool FP8, int NT>
-__global__ __launch_bounds__(256) void split_kernel(SplitArgs a)
+__global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(SplitArgs a)
 {
     using G = Geo<D, FP8>;
-    constexpr bool DBUF = 2 * G::RAW + NT * (G::STEPS + G::DB) * 4 <= 256;
+    constexpr int NBUF = Plan<D, FP8, NT>::NBUF;
+    constexpr int KT = G::KT;
     __shared__ int s_pre[kMaxSeq + 1];
+    __shared__ int s_len[kMaxSeq];
     __shared__ int s_tmp[256];
 
     const int S = a.n_seq, R = a.rows, Hk = a.n_head_kv, H = a.n_head;
@@ -326,7 +426,8 @@ __global__ __launch_bounds__(256) void split_kernel(SplitArgs a)
     const int64_t cap = (int64_t)a.max_pages * 16;
     const int tid = threadIdx.x;
 
-    // Exclusive prefix over sequences of their work items.
+    // Exclusive prefix over sequences of their work items, and the lengths
+    // (kept in LDS: item set-up then waits on no global load).
     {
         const int per = (S + 255) / 256;
         const int b0 = tid * per;
@@ -352,6 +453,7 @@ __global__ __launch_bounds__(256) void split_kernel(SplitArgs a)
             if (s < S) {
                 s_pre[s] = run;
                 const int C = a.ctx_lens[s];
+                s_len[s] = C;
                 run += ctx_ok(C, R, cap) ? ((C + kChunk - 1) / kChunk) * Hk : 0;
             }
         }
@@ -361,128 +463,154 @@ __global__ __launch_bounds__(256) void split_kernel(SplitArgs a)
     }
 
     const int lane = tid & 63, n = lane & 15, kb = lane >> 4;
-    const int total = s_pre[S];
+    // Wave-uniform values are made visibly uniform (scalar registers), so
+    // that loop bounds, page ids and buffer resources stay scalar.
+    const int total = __builtin_amdgcn_readfirstlane(s_pre[S]);
     const int nwaves = gridDim.x * kWaves;
     const float sm_log2 = kLog2e / __builtin_sqrtf((float)D);
     const uint8_t* __restrict__ kp = (const uint8_t*)a.k_pool;
     const uint8_t* __restrict__ vp = (const uint8_t*)a.v_pool;
+    const uint32_t koff = (uint32_t)(n * G::ROWB + 16 * kb);
+    const uint32_t voff = (uint32_t)(4 * kb * G::ROWB + n * G::VPB);
+    const __amdgpu_buffer_rsrc_t r_ks =
+        rsrc(a.k_scale, FP8 ? (uint32_t)(a.n_pages * Hk * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t r_vs =
+        rsrc(a.v_scale, FP8 ? (uint32_t)(a.n_pages * Hk * 4) : 0u);
 
-    for (int item = blockIdx.x * kWaves + (tid >> 6); item < total; item += nwaves) {
-        int lo = 0, hi = S - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_pre[mid] <= item)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int s = __builtin_amdgcn_readfirstlane(lo);
-        const int local = item - s_pre[s];
-        const int j = local / Hk, kh = local - j * Hk;
-        const int C = a.ctx_lens[s];
-        const int t0 = j * kChunk;
-        const int t1 = min(t0 + kChunk, C);
+    int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (tid >> 6));
+    if (item >= total)
+        return;
+    Item cur = resolve_item(s_pre, s_len, S, Hk, item);
+    int pid = fetch_pages(a, cur, true);
+    // A full wait (never too weak): the loop then finds pid resolved on
+    // entry as it does on every later iteration, and its compiler-placed
+    // waits need not cover this load.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    for (; item < total; item += nwaves) {
+        // Next item's table entries (a zero-length fetch past the end).
+        const int next = item + nwaves;
+        const Item nxt = resolve_item(s_pre, s_len, S, Hk, next < total ? next : item);
+        const int pid_next = fetch_pages(a, nxt, next < total);
+
+        const int s = cur.s, j = cur.j, kh = cur.kh, C = cur.C, t0 = cur.t0, t1 = cur.t1;
+        const int npg = cur.npg;
         const int cmr_mod = (C - R) % ppt;
-
-        // Pages of this item: lane i holds entry i (and its scales).
-        const int npg = (t1 - t0 + 15) >> 4;
-        int pid = -1;
-        float ksc = 0.f, vsc = 0.f;
-        if (lane < npg)
-            pid = a.block_table[(int64_t)s * a.max_pages + (t0 >> 4) + lane];
         const bool badp = lane < npg && (pid < 0 || (int64_t)pid >= a.n_pages);
         const bool bad = __builtin_amdgcn_ballot_w64(badp) != 0;
-        if (!bad && FP8 && lane < npg) {
-            ksc = a.k_scale[(int64_t)pid * Hk + kh];
-            vsc = a.v_scale[(int64_t)pid * Hk + kh];
+        // Scales of the item's pages, lane e for page e (0 past the item or
+        // for an entry outside the pool: the bounds check returns zero).
+        float ksc = 0.f, vsc = 0.f;
+        if constexpr (FP8) {
+            const uint32_t so = lane < npg && !badp ? (uint32_t)(pid * Hk + kh) * 4u : kFar;
+            ksc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ks, so, 0, 0));
+            vsc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_vs, so, 0, 0));
         }
 
+        // Query operands; empty slots read past the end of the query rows of
+        // s and get zeros.
         u32x4 qop[NT][G::STEPS];
         int last[NT];
         float m[NT], l[NT];
         f32x4 O[NT][G::DB];
+        {
+            const uint16_t* qs = (const uint16_t*)a.q + (int64_t)s * R * H * D;
+            const __amdgpu_buffer_rsrc_t rq = rsrc(qs, (uint32_t)(R * H * D * 2));
 #pragma unroll
-        for (int tau = 0; tau < NT; ++tau) {
-            const int r = slot_row(n, tau, g, ppt, R, cmr_mod);
-            last[tau] = r >= 0 ? C - R + r : -1;
-            const int h = kh * g + (n % g);
-            const uint16_t* qrow =
-                (const uint16_t*)a.q + (((int64_t)s * R + (r >= 0 ? r : 0)) * H + h) * D;
+            for (int tau = 0; tau < NT; ++tau) {
+                const int r = slot_row(n, tau, g, ppt, R, cmr_mod);
+                last[tau] = r >= 0 ? C - R + r : -1;
+                const int h = kh * g + (n % g);
+                const uint32_t qo = r >= 0 ? (uint32_t)((r * H + h) * D) * 2u : kFar;
 #pragma unroll
-            for (int st = 0; st < G::STEPS; ++st)
-                qop[tau][st] = r >= 0 ? *(const u32x4*)(qrow + qk_dmap<D, FP8>(st, kb))
-                                      : u32x4{0u, 0u, 0u, 0u};
-            m[tau] = neg_inf();
-            l[tau] = 0.f;
+                for (int st = 0; st < G::STEPS; ++st)
+                    qop[tau][st] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rq, qo + 2u * (uint32_t)qk_dmap<D, FP8>(st, kb), 0, 0);
+                m[tau] = neg_inf();
+                l[tau] = 0.f;
 #pragma unroll
-            for (int jb = 0; jb < G::DB; ++jb)
-                O[tau][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int jb = 0; jb < G::DB; ++jb)
+                    O[tau][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
 
         if (!bad) {
-            const int nt = (t1 - t0 + kKT - 1) / kKT;
-            auto page = [&](int e) { return e < npg ? __shfl(pid, e, 64) : 0; };
-            auto kscale = [&](int e) { return FP8 ? __shfl(ksc, e, 64) * sm_log2 : sm_log2; };
-            auto vscale = [&](int e) { return FP8 ? __shfl(vsc, e, 64) : 1.f; };
-            if constexpr (DBUF) {
-                Raw<D, FP8> A, B;
-                load_tile<D, FP8>(A, kp, vp, page(0), page(1), t0, C, Hk, kh, n, kb);
-                for (int it = 0; it < nt; it += 2) {
-                    if (it + 1 < nt)
-                        load_tile<D, FP8>(B, kp, vp, page(2 * it + 2), page(2 * it + 3),
-                                          t0 + kKT * (it + 1), C, Hk, kh, n, kb);
-                    compute_tile<D, FP8, NT>(A, qop, last, m, l, O, t0 + kKT * it,
-                                             kscale(2 * it), kscale(2 * it + 1), vscale(2 * it),
-                                             vscale(2 * it + 1), lane, kb);
-                    if (it + 1 < nt) {
-                        if (it + 2 < nt)
-                            load_tile<D, FP8>(A, kp, vp, page(2 * it + 4), page(2 * it + 5),
-                                              t0 + kKT * (it + 2), C, Hk, kh, n, kb);
-                        compute_tile<D, FP8, NT>(B, qop, last, m, l, O, t0 + kKT * (it + 1),
-                                                 kscale(2 * it + 2), kscale(2 * it + 3),
-                                                 vscale(2 * it + 2), vscale(2 * it + 3), lane, kb);
+            const int nt = (t1 - t0 + KT - 1) / KT;
+            // Chunk index and rows inside the item of page e (uniform).
+            auto chunk = [&](int e) -> int64_t {
+                const int p = e < npg ? rdlane(pid, e) : 0;
+                return (int64_t)p * Hk + kh;
+            };
+            // (readfirstlane keeps the clamp, which only the vector unit has,
+            // from turning the buffer resources into per-lane values.)
+            auto rows = [&](int e) {
+                return __builtin_amdgcn_readfirstlane(min(16, max(0, t1 - (t0 + 16 * e))));
+            };
+            auto issue = [&](Raw<D, FP8>& buf, int tile) {
+                const int e0 = tile * G::KB;
+                const int e1 = G::KB == 2 ? e0 + 1 : e0;
+                load_tile<D, FP8>(buf, kp, vp, chunk(e0), chunk(e1), rows(e0), rows(e1), koff,
+                                  voff);
+            };
+            auto kscale = [&](int e) {
+                return FP8 ? rdlane_f(ksc, e < npg ? e : 0) * sm_log2 : sm_log2;
+            };
+            auto vscale = [&](int e) { return FP8 ? rdlane_f(vsc, e < npg ? e : 0) : 1.f; };
+
+            Raw<D, FP8> buf[NBUF];
+#pragma unroll
+            for (int k = 0; k < NBUF - 1; ++k)
+                issue(buf[k], k);
+            for (int it = 0; it < nt; it += NBUF) {
+#pragma unroll
+                for (int k = 0; k < NBUF; ++k) {
+                    const int tile = it + k;
+                    issue(buf[(k + NBUF - 1) % NBUF], tile + NBUF - 1);
+                    if (tile < nt) {
+                        const int e0 = tile * G::KB;
+                        const int e1 = G::KB == 2 ? e0 + 1 : e0;
+                        compute_tile<D, FP8, NT>(buf[k], qop, last, m, l, O, t0 + KT * tile,
+                                                 kscale(e0), kscale(e1), vscale(e0), vscale(e1),
+                                                 kb);
                     }
-                }
-            } else {
-                Raw<D, FP8> A;
-                for (int it = 0; it < nt; ++it) {
-                    load_tile<D, FP8>(A, kp, vp, page(2 * it), page(2 * it + 1), t0 + kKT * it, C,
-                                      Hk, kh, n, kb);
-                    compute_tile<D, FP8, NT>(A, qop, last, m, l, O, t0 + kKT * it,
-                                             kscale(2 * it), kscale(2 * it + 1), vscale(2 * it),
-                                             vscale(2 * it + 1), lane, kb);
                 }
             }
         }
 
-        // Partials: O rows are slots 4*kb + r; m, l of slot n.
+        // Partials: O rows are slots 4*kb + r; m, l of slot n.  Bounds-checked
+        // stores: an empty slot stores at kFar, which the resource drops, so
+        // no store sits under a branch either.
         const float qnan = __builtin_nanf("");
+        const int64_t rec0 = ((int64_t)s * a.max_split + j) * R * H;  // record (s, j, row 0, head 0)
+        const __amdgpu_buffer_rsrc_t ro = rsrc(a.o_part + rec0 * D, (uint32_t)(R * H * D * 4));
+        const __amdgpu_buffer_rsrc_t rml = rsrc(a.ml_part + rec0 * 2, (uint32_t)(R * H * 2 * 4));
 #pragma unroll
         for (int tau = 0; tau < NT; ++tau) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int slot = 4 * kb + r;
                 const int row = slot_row(slot, tau, g, ppt, R, cmr_mod);
-                if (row >= 0) {
-                    const int h = kh * g + (slot % g);
-                    float* dst = a.o_part +
-                                 ((((int64_t)s * a.max_split + j) * R + row) * H + h) * D + n * G::DB;
+                const int h = kh * g + (slot % g);
+                const uint32_t off =
+                    row >= 0 ? (uint32_t)(((row * H + h) * D + n * G::DB) * 4) : kFar;
 #pragma unroll
-                    for (int jb = 0; jb < G::DB; jb += 4)
-                        *(f32x4*)(dst + jb) =
-                            bad ? f32x4{qnan, qnan, qnan, qnan}
-                                : f32x4{O[tau][jb][r], O[tau][jb + 1][r], O[tau][jb + 2][r],
-                                        O[tau][jb + 3][r]};
+                for (int jb = 0; jb < G::DB; jb += 4) {
+                    const f32x4 v = bad ? f32x4{qnan, qnan, qnan, qnan}
+                                        : f32x4{O[tau][jb][r], O[tau][jb + 1][r],
+                                                O[tau][jb + 2][r], O[tau][jb + 3][r]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                                           off + 4u * jb, 0, 0);
                 }
             }
             const int row = slot_row(n, tau, g, ppt, R, cmr_mod);
-            if (kb == 0 && row >= 0) {
-                const int h = kh * g + (n % g);
-                float* dst = a.ml_part + ((((int64_t)s * a.max_split + j) * R + row) * H + h) * 2;
-                dst[0] = bad ? qnan : m[tau];
-                dst[1] = bad ? qnan : l[tau];
-            }
+            const int h = kh * g + (n % g);
+            const uint32_t off = (kb == 0 && row >= 0) ? (uint32_t)((row * H + h) * 8) : kFar;
+            const f32x2 v = bad ? f32x2{qnan, qnan} : f32x2{m[tau], l[tau]};
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rml, off, 0, 0);
         }
+
+        cur = nxt;
+        pid = pid_next;
     }
 }
 
@@ -514,25 +642,61 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
     const float* op = a.o_part + (((int64_t)s * a.max_split * R + r) * H + h) * D + lane * E;
     const int64_t mls = (int64_t)R * H * 2, ops = (int64_t)R * H * D;  // per-split strides
 
+    // Splits in groups of 64, lane = split within the group.
     float M = neg_inf();
     bool nan = false;
-    for (int j = 0; j < ns; ++j) {
-        const float mj = ml[j * mls];
+    for (int j0 = 0; j0 < ns; j0 += 64) {
+        const int jj = j0 + lane;
+        const float mj = jj < ns ? ml[jj * mls] : neg_inf();
         nan |= mj != mj;
         M = fmaxf(M, mj);
     }
+    nan = __builtin_amdgcn_ballot_w64(nan) != 0;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1)
+        M = fmaxf(M, shfl_xor_f(M, k));
+
     float num[E], den = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e)
         num[e] = 0.f;
-    for (int j = 0; j < ns; ++j) {
-        const float mj = ml[j * mls], lj = ml[j * mls + 1];
-        const float wj = mj == M ? 1.f : __builtin_amdgcn_exp2f(mj - M);
-        den = den + wj * lj;
-        const float* oj = op + j * ops;
+    for (int j0 = 0; j0 < ns; j0 += 64) {
+        const int jj = j0 + lane;
+        float wj = 0.f, lj = 0.f;
+        if (jj < ns) {
+            const f32x2 v = *(const f32x2*)(ml + jj * mls);
+            wj = v[0] == M ? 1.f : __builtin_amdgcn_exp2f(v[0] - M);
+            lj = v[1];
+        }
+        float dl = wj * lj;
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            num[e] = num[e] + wj * oj[e];
+        for (int k = 1; k < 64; k <<= 1)
+            dl = dl + shfl_xor_f(dl, k);
+        den = den + dl;
+        const int cnt = min(64, ns - j0);
+        const float* o0 = op + (int64_t)j0 * ops;
+        int q = 0;
+        for (; q + 8 <= cnt; q += 8) {
+            float ov[8][E];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    ov[u][e] = o0[(int64_t)(q + u) * ops + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wu = rdlane_f(wj, q + u);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    num[e] = num[e] + wu * ov[u][e];
+            }
+        }
+        for (; q < cnt; ++q) {
+            const float wu = rdlane_f(wj, q);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                num[e] = num[e] + wu * o0[(int64_t)q * ops + e];
+        }
     }
 #pragma unroll
     for (int e = 0; e < E; ++e)
