@@ -247,6 +247,15 @@ const char* attn_last_error(void);
  */
 void attn_set_kernel_timer(hipEvent_t start, hipEvent_t stop);
 
+/*
+ * Upper bound on the workgroups of the decode / verify attention kernel for
+ * every later call in the process (0, the default, lets the grid fill the
+ * device; negative values count as 0).  The kernel's waves walk the work
+ * items whatever their number, and results do not depend on it, so a small
+ * bound lets tests drive many work items through each wave on small inputs.
+ */
+void attn_set_max_workgroups(int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

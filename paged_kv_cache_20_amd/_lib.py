@@ -35,7 +35,7 @@ EXPORTS = [
     "attn_paged_decode", "attn_paged_verify", "attn_paged_prefill", "attn_kv_append",
     "attn_block_table_build", "attn_paged_workspace_bytes", "attn_caps",
     "attn_check_lengths_host", "attn_check_block_table_host", "attn_last_error",
-    "attn_set_kernel_timer",
+    "attn_set_kernel_timer", "attn_set_max_workgroups",
 ]
 
 
@@ -82,6 +82,8 @@ _lib.attn_last_error.argtypes = []
 _lib.attn_last_error.restype = ctypes.c_char_p
 _lib.attn_set_kernel_timer.argtypes = [_P, _P]
 _lib.attn_set_kernel_timer.restype = None
+_lib.attn_set_max_workgroups.argtypes = [_I32]
+_lib.attn_set_max_workgroups.restype = None
 
 
 def lib() -> ctypes.CDLL:
@@ -208,3 +210,9 @@ def attn_set_kernel_timer(start_event, stop_event) -> None:
             return e
         return e.cuda_event if hasattr(e, "cuda_event") else e.event_id
     _lib.attn_set_kernel_timer(h(start_event), h(stop_event))
+
+
+def attn_set_max_workgroups(n: int) -> None:
+    """Bound the decode/verify kernel's grid for later calls (0 = fill the
+    device); results do not depend on it."""
+    _lib.attn_set_max_workgroups(int(n))

@@ -9,6 +9,7 @@
 // section "Probe: what the plugin measured").
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -25,6 +26,7 @@ namespace {
 thread_local char t_err[256] = "";
 thread_local hipEvent_t t_ev_start = nullptr;
 thread_local hipEvent_t t_ev_stop = nullptr;
+std::atomic<int32_t> g_max_workgroups{0};
 
 int fail(int code, const char* fmt, ...)
 {
@@ -184,6 +186,7 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     a.ev_start = t_ev_start;
     a.ev_stop = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
+    a.max_blocks = g_max_workgroups.load(std::memory_order_relaxed);
     return from_hip(pa::launch_split_decode(a, stream), fn);
 }
 
@@ -197,6 +200,11 @@ void attn_set_kernel_timer(hipEvent_t start, hipEvent_t stop)
 {
     t_ev_start = start;
     t_ev_stop = stop;
+}
+
+void attn_set_max_workgroups(int32_t n)
+{
+    g_max_workgroups.store(n > 0 ? n : 0, std::memory_order_relaxed);
 }
 
 int attn_caps(int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype)

@@ -147,6 +147,10 @@ struct Plan {
     static constexpr int OCC = (2 * RAW + QOP + OREG <= 176) ? 2 : 1;
     static constexpr int NBUF = OCC == 2 ? ((3 * RAW + QOP + OREG <= 160) ? 3 : 2)
                                          : ((3 * RAW + QOP <= 224) ? 3 : 2);
+    // Whether the next item's query operands are loaded into a second set of
+    // registers during the current item's last tiles (one slot tile only;
+    // larger calls load them after the current item's last tile).
+    static constexpr bool PREQ = NT == 1;
 };
 
 // Element offset (in the query row) of the first of the 8 d-values that
@@ -416,6 +420,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
 {
     using G = Geo<D, FP8>;
     constexpr int NBUF = Plan<D, FP8, NT>::NBUF;
+    constexpr bool PREQ = Plan<D, FP8, NT>::PREQ;
     constexpr int KT = G::KT;
     __shared__ int s_pre[kMaxSeq + 1];
     __shared__ int s_len[kMaxSeq];
@@ -477,104 +482,148 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     const __amdgpu_buffer_rsrc_t r_vs =
         rsrc(a.v_scale, FP8 ? (uint32_t)(a.n_pages * Hk * 4) : 0u);
 
+    // Page e of item I: its (page, kv head) chunk and its rows inside the
+    // item.  An entry outside the pool, a page past the item and a dead item
+    // give chunk 0 with no rows, so no load can leave the pool.
+    auto page = [&](const Item& I, int pidv, bool live, int e, int64_t& chunk, int& rows) {
+        const int p = rdlane(pidv, e);
+        const bool ok = live && e < I.npg && p >= 0 && (int64_t)p < a.n_pages;
+        chunk = (int64_t)(ok ? p : 0) * Hk + I.kh;
+        // (readfirstlane keeps the clamp, which only the vector unit has,
+        // from turning the buffer resources into per-lane values.)
+        rows = ok ? __builtin_amdgcn_readfirstlane(min(16, max(0, I.t1 - (I.t0 + 16 * e)))) : 0;
+    };
+    auto issue = [&](Raw<D, FP8>& buf, const Item& I, int pidv, bool live, int tile) {
+        const int e0 = tile * G::KB;
+        const int e1 = G::KB == 2 ? e0 + 1 : e0;
+        int64_t c0, c1;
+        int r0, r1;
+        page(I, pidv, live, e0, c0, r0);
+        page(I, pidv, live, e1, c1, r1);
+        load_tile<D, FP8>(buf, kp, vp, c0, c1, r0, r1, koff, voff);
+    };
+    // Query operands of item I; empty slots read past the end of the query
+    // rows of I's sequence and get zeros.
+    auto load_q = [&](u32x4 (&qd)[NT][G::STEPS], const Item& I, bool live) {
+        const uint16_t* qs = (const uint16_t*)a.q + (int64_t)I.s * R * H * D;
+        const __amdgpu_buffer_rsrc_t rq = rsrc(qs, live ? (uint32_t)(R * H * D * 2) : 0u);
+        const int cm = (I.C - R) % ppt;
+        const int h = I.kh * g + (n % g);
+#pragma unroll
+        for (int tau = 0; tau < NT; ++tau) {
+            const int r = slot_row(n, tau, g, ppt, R, cm);
+            const uint32_t qo = r >= 0 ? (uint32_t)((r * H + h) * D) * 2u : kFar;
+#pragma unroll
+            for (int st = 0; st < G::STEPS; ++st)
+                qd[tau][st] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rq, qo + 2u * (uint32_t)qk_dmap<D, FP8>(st, kb), 0, 0);
+        }
+    };
+    // Scales of item I's pages, lane e for page e (zero past the item, for
+    // an entry outside the pool, and for bf16).
+    auto load_scales = [&](float& ks, float& vs, const Item& I, int pidv, bool live) {
+        ks = vs = 0.f;
+        if constexpr (FP8) {
+            const bool ok = live && lane < I.npg && pidv >= 0 && (int64_t)pidv < a.n_pages;
+            const uint32_t so = ok ? (uint32_t)(pidv * Hk + I.kh) * 4u : kFar;
+            ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ks, so, 0, 0));
+            vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_vs, so, 0, 0));
+        }
+    };
+
     int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (tid >> 6));
     if (item >= total)
         return;
+
+    // The wave's tiles form one stream over its items: the ring's loads run
+    // NBUF - 1 tiles ahead of the compute, across item boundaries.  Items
+    // are padded to a multiple of NBUF tiles (padding tiles load nothing and
+    // are not computed), so every item starts at ring slot 0.
+    // Table entries are fetched two items ahead and held in registers one
+    // item ahead, so the ring never waits for them.
     Item cur = resolve_item(s_pre, s_len, S, Hk, item);
     int pid = fetch_pages(a, cur, true);
-    // A full wait (never too weak): the loop then finds pid resolved on
-    // entry as it does on every later iteration, and its compiler-placed
-    // waits need not cover this load.
+    bool has_next = item + nwaves < total;
+    Item nxt = resolve_item(s_pre, s_len, S, Hk, has_next ? item + nwaves : item);
+    int pid_n = fetch_pages(a, nxt, has_next);
+    // A full wait (never too weak): the loop then finds pid and pid_n
+    // resolved on entry as it does on every later iteration, and its
+    // compiler-placed waits need not cover these loads.
     __builtin_amdgcn_s_waitcnt(0);
+    u32x4 qop[NT][G::STEPS];
+    float ksc, vsc;
+    load_q(qop, cur, true);
+    load_scales(ksc, vsc, cur, pid, true);
+    Raw<D, FP8> buf[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+        issue(buf[k], cur, pid, true, k);
 
-    for (; item < total; item += nwaves) {
-        // Next item's table entries (a zero-length fetch past the end).
-        const int next = item + nwaves;
-        const Item nxt = resolve_item(s_pre, s_len, S, Hk, next < total ? next : item);
-        const int pid_next = fetch_pages(a, nxt, next < total);
+    for (;;) {
+        // The item after next: geometry and table entries now.
+        const int next2 = item + 2 * nwaves;
+        const bool has_next2 = next2 < total;
+        const Item nxt2 = resolve_item(s_pre, s_len, S, Hk, has_next2 ? next2 : item);
+        const int pid_nn = fetch_pages(a, nxt2, has_next2);
 
         const int s = cur.s, j = cur.j, kh = cur.kh, C = cur.C, t0 = cur.t0, t1 = cur.t1;
         const int npg = cur.npg;
         const int cmr_mod = (C - R) % ppt;
         const bool badp = lane < npg && (pid < 0 || (int64_t)pid >= a.n_pages);
         const bool bad = __builtin_amdgcn_ballot_w64(badp) != 0;
-        // Scales of the item's pages, lane e for page e (0 past the item or
-        // for an entry outside the pool: the bounds check returns zero).
-        float ksc = 0.f, vsc = 0.f;
-        if constexpr (FP8) {
-            const uint32_t so = lane < npg && !badp ? (uint32_t)(pid * Hk + kh) * 4u : kFar;
-            ksc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ks, so, 0, 0));
-            vsc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_vs, so, 0, 0));
-        }
+        const int nt = (t1 - t0 + KT - 1) / KT;
+        const int ntp = (nt + NBUF - 1) / NBUF * NBUF;
 
-        // Query operands; empty slots read past the end of the query rows of
-        // s and get zeros.
-        u32x4 qop[NT][G::STEPS];
         int last[NT];
         float m[NT], l[NT];
         f32x4 O[NT][G::DB];
-        {
-            const uint16_t* qs = (const uint16_t*)a.q + (int64_t)s * R * H * D;
-            const __amdgpu_buffer_rsrc_t rq = rsrc(qs, (uint32_t)(R * H * D * 2));
 #pragma unroll
-            for (int tau = 0; tau < NT; ++tau) {
-                const int r = slot_row(n, tau, g, ppt, R, cmr_mod);
-                last[tau] = r >= 0 ? C - R + r : -1;
-                const int h = kh * g + (n % g);
-                const uint32_t qo = r >= 0 ? (uint32_t)((r * H + h) * D) * 2u : kFar;
+        for (int tau = 0; tau < NT; ++tau) {
+            const int r = slot_row(n, tau, g, ppt, R, cmr_mod);
+            last[tau] = r >= 0 ? C - R + r : -1;
+            m[tau] = neg_inf();
+            l[tau] = 0.f;
 #pragma unroll
-                for (int st = 0; st < G::STEPS; ++st)
-                    qop[tau][st] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rq, qo + 2u * (uint32_t)qk_dmap<D, FP8>(st, kb), 0, 0);
-                m[tau] = neg_inf();
-                l[tau] = 0.f;
+            for (int jb = 0; jb < G::DB; ++jb)
+                O[tau][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        auto kscale = [&](int e) {
+            return FP8 ? rdlane_f(ksc, e < npg ? e : 0) * sm_log2 : sm_log2;
+        };
+        auto vscale = [&](int e) { return FP8 ? rdlane_f(vsc, e < npg ? e : 0) : 1.f; };
+        auto compute = [&](const Raw<D, FP8>& t, int tile) {
+            const int e0 = tile * G::KB;
+            const int e1 = G::KB == 2 ? e0 + 1 : e0;
+            compute_tile<D, FP8, NT>(t, qop, last, m, l, O, t0 + KT * tile, kscale(e0),
+                                     kscale(e1), vscale(e0), vscale(e1), kb);
+        };
+
+        // Tiles whose ring successor is still in this item.
+        for (int it = 0; it < ntp - NBUF; it += NBUF) {
 #pragma unroll
-                for (int jb = 0; jb < G::DB; ++jb)
-                    O[tau][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < NBUF; ++k) {
+                const int tile = it + k;
+                issue(buf[(k + NBUF - 1) % NBUF], cur, pid, true, tile + NBUF - 1);
+                if (!bad && tile < nt)
+                    compute(buf[k], tile);
             }
         }
-
-        if (!bad) {
-            const int nt = (t1 - t0 + KT - 1) / KT;
-            // Chunk index and rows inside the item of page e (uniform).
-            auto chunk = [&](int e) -> int64_t {
-                const int p = e < npg ? rdlane(pid, e) : 0;
-                return (int64_t)p * Hk + kh;
-            };
-            // (readfirstlane keeps the clamp, which only the vector unit has,
-            // from turning the buffer resources into per-lane values.)
-            auto rows = [&](int e) {
-                return __builtin_amdgcn_readfirstlane(min(16, max(0, t1 - (t0 + 16 * e))));
-            };
-            auto issue = [&](Raw<D, FP8>& buf, int tile) {
-                const int e0 = tile * G::KB;
-                const int e1 = G::KB == 2 ? e0 + 1 : e0;
-                load_tile<D, FP8>(buf, kp, vp, chunk(e0), chunk(e1), rows(e0), rows(e1), koff,
-                                  voff);
-            };
-            auto kscale = [&](int e) {
-                return FP8 ? rdlane_f(ksc, e < npg ? e : 0) * sm_log2 : sm_log2;
-            };
-            auto vscale = [&](int e) { return FP8 ? rdlane_f(vsc, e < npg ? e : 0) : 1.f; };
-
-            Raw<D, FP8> buf[NBUF];
+        // The item's last NBUF tiles; the ring moves on to the next item,
+        // whose scales (and query rows) are loaded first.
+        u32x4 qop_n[PREQ ? NT : 1][G::STEPS];
+        float ksc_n, vsc_n;
+        if constexpr (PREQ)
+            load_q(qop_n, nxt, has_next);
+        load_scales(ksc_n, vsc_n, nxt, pid_n, has_next);
 #pragma unroll
-            for (int k = 0; k < NBUF - 1; ++k)
-                issue(buf[k], k);
-            for (int it = 0; it < nt; it += NBUF) {
-#pragma unroll
-                for (int k = 0; k < NBUF; ++k) {
-                    const int tile = it + k;
-                    issue(buf[(k + NBUF - 1) % NBUF], tile + NBUF - 1);
-                    if (tile < nt) {
-                        const int e0 = tile * G::KB;
-                        const int e1 = G::KB == 2 ? e0 + 1 : e0;
-                        compute_tile<D, FP8, NT>(buf[k], qop, last, m, l, O, t0 + KT * tile,
-                                                 kscale(e0), kscale(e1), vscale(e0), vscale(e1),
-                                                 kb);
-                    }
-                }
-            }
+        for (int k = 0; k < NBUF; ++k) {
+            const int tile = ntp - NBUF + k;
+            if (k == 0)
+                issue(buf[NBUF - 1], cur, pid, true, ntp - 1);
+            else
+                issue(buf[k - 1], nxt, pid_n, has_next, k - 1);
+            if (!bad && tile < nt)
+                compute(buf[k], tile);
         }
 
         // Partials: O rows are slots 4*kb + r; m, l of slot n.  Bounds-checked
@@ -609,8 +658,25 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rml, off, 0, 0);
         }
 
+        if (!has_next)
+            break;
+        item += nwaves;
         cur = nxt;
-        pid = pid_next;
+        pid = pid_n;
+        nxt = nxt2;
+        pid_n = pid_nn;
+        has_next = has_next2;
+        if constexpr (PREQ) {
+#pragma unroll
+            for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+                for (int st = 0; st < G::STEPS; ++st)
+                    qop[tau][st] = qop_n[tau][st];
+        } else {
+            load_q(qop, cur, true);
+        }
+        ksc = ksc_n;
+        vsc = vsc_n;
     }
 }
 
@@ -727,6 +793,8 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
     int64_t blocks = (upper + kWaves - 1) / kWaves;
     if (blocks > grid_cap)
         blocks = grid_cap;
+    if (a.max_blocks > 0 && blocks > a.max_blocks)
+        blocks = a.max_blocks;
     if (blocks < 1)
         blocks = 1;
     if (a.ev_start)

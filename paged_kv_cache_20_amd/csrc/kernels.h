@@ -37,6 +37,7 @@ struct SplitArgs {
     float* ml_part;  // [n_seq][max_split][rows][n_head][2]
     int32_t max_split;
     hipEvent_t ev_start, ev_stop;  // optional timing pair around the split kernel
+    int32_t max_blocks;            // grid bound for the split kernel; 0 = fill the device
 };
 
 // Decode (rows = 1) and verify (rows = 8): split kernel + fixed-order combine.

@@ -62,6 +62,19 @@ def test_small_parity(small):
     assert excess_err(out, ref, TOL[w.kv_fp8]) <= 0
 
 
+def test_one_workgroup_walks_every_item_bitwise(small):
+    """With the grid bound to one workgroup, each wave walks many work items
+    (the ring runs across item boundaries); output must not change by a bit."""
+    w, inp, gpu, out = small
+    pa.attn_set_max_workgroups(1)
+    try:
+        one = gpu.run(w.kind)
+        torch.cuda.synchronize()
+    finally:
+        pa.attn_set_max_workgroups(0)
+    assert same_bits(one, out)
+
+
 def test_small_determinism(small):
     w, inp, gpu, out = small
     again = gpu.run(w.kind)
