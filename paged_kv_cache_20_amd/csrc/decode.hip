@@ -136,17 +136,24 @@ struct Raw {
 
 // Register plan of an instantiation: waves per SIMD it is compiled for
 // (two where two tiles, Q and O fit in half the register file) and the depth
-// of its tile ring (three tiles where they fit beside Q and O).  With one
-// wave per SIMD the O accumulators live in the AGPR half of the file.
+// of its tile ring.  Items are padded to a multiple of the depth; padding
+// tiles load nothing, so p of them at an item's end leave the ring NBUF - 1 - p
+// real tiles ahead of the item's last tile.  Depth 4 (no padding for a full
+// item of 16 or 32 tiles) where four tiles fit beside Q and O; with one wave
+// per SIMD, depth 3 where a full item has 32 tiles (one padding tile); else
+// depth 2 (no padding).  With one wave per SIMD the O accumulators live in
+// the AGPR half of the file.
 template <int D, bool FP8, int NT>
 struct Plan {
     using G = Geo<D, FP8>;
     static constexpr int RAW = G::KB * G::KLD * 4 + G::KEYS * G::VDW;  // dwords per tile
     static constexpr int QOP = NT * G::STEPS * 4;
     static constexpr int OREG = NT * G::DB * 4;
+    static constexpr int ITEM_TILES = kChunk / G::KT;
     static constexpr int OCC = (2 * RAW + QOP + OREG <= 176) ? 2 : 1;
-    static constexpr int NBUF = OCC == 2 ? ((3 * RAW + QOP + OREG <= 160) ? 3 : 2)
-                                         : ((3 * RAW + QOP <= 224) ? 3 : 2);
+    static constexpr int NBUF =
+        OCC == 2 ? ((4 * RAW + 2 * QOP + OREG <= 192) ? 4 : 2)
+                 : ((ITEM_TILES % 3 == 2 && 3 * RAW + QOP <= 224) ? 3 : 2);
     // Whether the next item's query operands are loaded into a second set of
     // registers during the current item's last tiles (one slot tile only;
     // larger calls load them after the current item's last tile).
