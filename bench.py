@@ -3,6 +3,8 @@
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-secondary] [--no-cpu]
+  python bench.py --calibration
+
 
 Prints ONE JSON line.  The headline workload is the fp8-KV decode step at
 256 sequences (n_head 32, n_head_kv 8, head_dim 128, page 16, contexts
@@ -16,6 +18,13 @@ single-sequence decode (latency), 64-sequence bf16 decode at head_dim 256,
 the 8-row verify round, and the 4096-row prefill chunk (bf16 MFMA TFLOP/s).
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the headline
 workload on this host.
+
+`roofline.traffic` is the measured HBM bytes per launch of the timed kernel,
+read from profiles/hbm_traffic.json when that file was taken on the current
+kernel sources (else null).  It comes from rocprofv3 FETCH_SIZE and
+WRITE_SIZE passes over this script, each scaled by what the same counter
+reads for `--calibration`, which runs two kernels of known traffic: a fill
+that writes 1 GiB and a sum that reads 1 GiB.
 """
 from __future__ import annotations
 
@@ -279,7 +288,19 @@ def main():
     ap.add_argument("--workload", default="decode_256seq_fp8")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibration", action="store_true",
+                    help="run a 1 GiB fill and a 1 GiB sum (counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibration:
+        import torch
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        s = None
+        for _ in range(3):
+            x.fill_(1.0)   # writes 1 GiB
+            s = x.sum()    # reads 1 GiB
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "fill 1 GiB, sum 1 GiB", "sum": float(s)}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d refused)" % args.gpus, file=sys.stderr)
