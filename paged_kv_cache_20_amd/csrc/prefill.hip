@@ -30,8 +30,9 @@
 //                                  re-packed in place; O^T's row is again
 //                                  the lane's row, so rescaling and 1/l are
 //                                  lane-local
-//   The row max only moves when a score exceeds it by more than 2^8, so O is
-//   rarely rescaled (P stays <= 2^8).
+//   The row max only moves when a score of the tile exceeds it by more than
+//   2^8 (checked once per tile, before any of its scores becomes a
+//   probability), so O is rarely rescaled (P stays <= 2^8).
 //   Workgroups of one kv head are placed on the same XCDs (blockIdx mod 8
 //   picks the XCD) so the K/V tiles they stream share that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -400,10 +401,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
                         acc[kq], 0, 0, 0);
             }
         };
-        auto check_half = [&](int hf) {
+        // One max check over the whole tile, before any of its scores is
+        // turned into a probability: a rescale between the two halves would
+        // leave the first half's P relative to the old max.
+        auto check_tile = [&]() {
             float tmax = neg_inf();
 #pragma unroll
-            for (int kq = 2 * hf; kq < 2 * hf + 2; ++kq) {
+            for (int kq = 0; kq < 4; ++kq) {
                 const float s = FP8 ? sc[kq] * sm_log2 : sm_log2;
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
@@ -474,10 +478,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             }
         };
         s_half(0);
-        check_half(0);
         s_half(1);
+        check_tile();
         softmax_half(0);
-        check_half(1);
         pv_half(0);
         softmax_half(1);
         pv_half(1);

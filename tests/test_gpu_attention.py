@@ -284,3 +284,26 @@ def test_full_workload_sampled_parity(name, k):
             assert same_bits(dec[:, 0], out[:, r])
     del gpu, inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", ["decode", "verify"])
+def test_score_jump_inside_tile(kind):
+    """Keys [40, 56) score 11.3 (q = k = 1 at head_dim 128), the rest 0, with
+    V = -1 there and +1 elsewhere: the row max jumps by more than 2^8 inside
+    one key tile."""
+    rows = 1 if kind == "decode" else 8
+    w = synth.listed("jump_" + kind, [90, 300], rows, 8, 2, 128, False, 51, kind=kind)
+    inp = synth.draw(w, "cuda")
+    k = torch.zeros_like(inp.k_src)
+    v = torch.ones_like(inp.v_src)
+    for s0 in (0, 90):  # both sequences' tokens
+        k[s0 + 40:s0 + 56] = 1.0
+        v[s0 + 40:s0 + 56] = -1.0
+    inp.k_src, inp.v_src = k, v
+    inp.q = torch.ones_like(inp.q)
+    gpu = GpuCache(inp)
+    out = gpu.run(kind)
+    torch.cuda.synchronize()
+    ref = OracleCache(inp).attend(inp.q)
+    say("[gpu] score jump", kind, "max abs err", max_err(out, ref))
+    assert excess_err(out, ref, TOL[False]) <= 0

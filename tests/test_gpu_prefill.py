@@ -87,3 +87,30 @@ def test_prefill_full_chunk_sampled_rows():
     assert err <= TOL[False]
     del gpu, inp
     torch.cuda.empty_cache()
+
+
+def _score_jump_inputs(w, lo, hi):
+    """Keys [lo, hi) score 11.3 (q = k = 1 at head_dim 128), every other key
+    scores 0; V is +1 on the other keys and -1 on [lo, hi).  The row max
+    jumps by more than 2^8 inside one key tile, so a tile's rescale must
+    cover all of its scores."""
+    inp = synth.draw(w, "cuda")
+    k = torch.zeros_like(inp.k_src)
+    v = torch.ones_like(inp.v_src)
+    k[lo:hi] = 1.0
+    v[lo:hi] = -1.0
+    inp.k_src, inp.v_src = k, v
+    inp.q = torch.ones_like(inp.q)
+    return inp
+
+
+@pytest.mark.parametrize("lo,hi", [(32, 64), (48, 64), (16, 32), (100, 130)])
+def test_prefill_score_jump_inside_tile(lo, hi):
+    w = prefill_case("pf_jump", 8, 160, 8, 2, 128, False, 50)
+    inp = _score_jump_inputs(w, lo, hi)
+    gpu = GpuCache(inp)
+    out = gpu.run("prefill")
+    torch.cuda.synchronize()
+    ref = OracleCache(inp).attend(inp.q)
+    say("[gpu] prefill score jump", lo, hi, "max abs err", max_err(out, ref))
+    assert excess_err(out, ref, TOL[False]) <= 0
