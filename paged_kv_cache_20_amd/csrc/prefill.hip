@@ -5,34 +5,38 @@
 // 0 .. that position.
 //
 // Work decomposition (gfx950)
-//   A workgroup of 8 waves owns one kv head and 128 query rows: 128/g
-//   consecutive positions x the g query heads that share the kv head, so
-//   every K/V tile it stages serves g heads.  Wave w owns rows 16w..16w+15,
-//   which keeps a wave's Q (32 VGPRs) and O (64 accumulators) small enough
-//   for two waves per SIMD: one wave's matrix work overlaps the other's
-//   softmax.
-//   Keys stream in 64-key tiles (four 16-token pages) through two LDS
-//   buffers, K and V both row-major as bf16 with each row's 16-byte chunks
+//   A workgroup of NW waves owns one kv head and 16 RT NW query rows:
+//   that many rows / g consecutive positions x the g query heads sharing the
+//   kv head, so every K/V tile it stages serves g heads.  Wave w owns RT
+//   16-row tiles (rows 16 (RT w + rt) + 0..15); each K or V operand read from
+//   LDS feeds RT matrix instructions.
+//   Keys stream in 64-key tiles (four 16-token pages).  K and V tiles live in
+//   two LDS buffers each, row-major as bf16 with each row's 16-byte chunks
 //   XOR-swizzled by the row index (conflict-free reads of a column of rows).
 //   bf16 pages are copied global -> LDS by buffer loads that write LDS
 //   directly (no registers in flight); the buffer descriptor of each page
 //   covers only the rows below ctx_len, so rows past the context arrive as
 //   zeros.  fp8 pages are loaded into registers, converted to bf16 exactly
 //   and written to the same layout.
+//   Software pipeline: the scores of tile t+1 are computed while tile t's
+//   softmax runs, so the matrix unit has independent work during the
+//   exponentials.  Iteration t therefore reads K(t+1) and V(t) and fills
+//   K(t+2) and V(t+1) into the buffers K(t) and V(t-1) left free.
 //   Per wave and tile, on v_mfma_f32_16x16x32_bf16:
 //     S^T[key][row] = K . Q^T      K rows by ds_read_b128, Q^T in registers
 //     online softmax               a row's 16 scores of the tile sit in the 4
-//                                  lanes row + 16 j, so max and sum take two
-//                                  cross-lane swaps
+//                                  lanes row + 16 j; each lane keeps its own
+//                                  part of the row sum, and the row max is
+//                                  only gathered across the 4 lanes when a
+//                                  lane's score exceeds it by more than 2^8
+//                                  (checked once per tile, before any score of
+//                                  the tile becomes a probability)
 //     O^T[d][row]  += V^T . P^T    V^T by ds_read_b64_tr_b16 (a 4-key x
 //                                  16-column block per 16 lanes, transposed
 //                                  in the read); P^T is the S^T accumulator
 //                                  re-packed in place; O^T's row is again
 //                                  the lane's row, so rescaling and 1/l are
 //                                  lane-local
-//   The row max only moves when a score of the tile exceeds it by more than
-//   2^8 (checked once per tile, before any of its scores becomes a
-//   probability), so O is rarely rescaled (P stays <= 2^8).
 //   Workgroups of one kv head are placed on the same XCDs (blockIdx mod 8
 //   picks the XCD) so the K/V tiles they stream share that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -40,11 +44,13 @@
 
 #include "kernels.h"
 
+
 namespace pa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -54,22 +60,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKT = 64;       // keys per tile
-constexpr int kWaves = 8;     // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
 constexpr int kRsrcFlags = 0x00020000;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
-__device__ __forceinline__ uint32_t bf16_bits(float x)
-{
-    __bf16 b = (__bf16)x;
-    return (uint32_t)__builtin_bit_cast(uint16_t, b);
-}
-
+// Two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
-    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 template <bool HI>
@@ -91,22 +90,27 @@ __device__ __forceinline__ int swz(int r)
            ((((r >> 2) ^ (r >> 3)) & 1) << 3);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int RT, int NW>
 struct PGeo {
+    static constexpr int NTH = 64 * NW;          // threads per workgroup
+    static constexpr int ROWS = 16 * RT * NW;    // query rows per workgroup
     static constexpr int EB = FP8 ? 1 : 2;
     static constexpr int ROWB = D * EB;          // bytes of one token row in the pool
     static constexpr int ROWL = D * 2;           // bytes of one row in LDS (bf16)
     static constexpr int CPRL = ROWL / 16;       // 16-byte chunks per LDS row
     static constexpr int TILEB = kKT * ROWL;     // one K (or V) tile in LDS
-    static constexpr int BUF = 2 * TILEB + 64;   // K, V, per-page scales
     static constexpr int KSTEPS = D / 32;        // k-steps of QK^T
     static constexpr int DBLK = D / 16;          // 16-wide d blocks of O^T
     // direct (bf16) loads: 1 KiB LDS blocks
     static constexpr int RPB = 1024 / ROWL;            // rows per block
-    static constexpr int NBW = (kKT / RPB) / kWaves;   // blocks per wave per tensor
-    // staged (fp8) loads: 16-byte pool chunks per thread per tensor
+    static constexpr int NBW = (kKT / RPB) / NW;       // blocks per wave per tensor
+    // Each wave loads KPW consecutive keys of a tile, all in one page.
+    static constexpr int KPW = kKT / NW;
+    // staged (fp8) loads: 16-byte pool chunks per lane per tensor
     static constexpr int CPR = ROWB / 16;
-    static constexpr int SCH = kKT * CPR / kThreads;
+    static constexpr int SCH = KPW * CPR / 64;
+    static_assert(NBW * RPB == KPW && KPW <= 16, "direct loads: one page per wave");
+    static_assert(SCH * 64 == KPW * CPR, "staged loads must cover the wave's keys");
 };
 
 struct Blk {
@@ -115,150 +119,144 @@ struct Blk {
     const int32_t* bt;
 };
 
-// Block-table entries of the tile at tile0 (raw, not yet checked); -1 past
-// the context.  Issued a tile ahead so their latency hides behind compute.
-__device__ __forceinline__ void fetch_pages(const Blk& b, int tile0, int (&raw)[4])
+// Block-table entry of the page holding keys key0 .. key0 + 15 (raw, not yet
+// checked); -1 past the context.  Issued tiles ahead so its latency hides
+// behind compute.
+__device__ __forceinline__ int fetch_page(const Blk& b, int key0)
 {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int key0 = tile0 + 16 * q;
-        raw[q] = key0 < b.C ? b.bt[key0 >> 4] : -1;
-    }
+    return key0 < b.C ? b.bt[key0 >> 4] : -1;
 }
 
-// Page of the q-th 16-key group of the tile at tile0 and the number of its
-// rows below the context; page -1 (and 0 rows) past the context or for an
-// entry outside the pool (which also raises *bad).
-__device__ __forceinline__ void resolve_pages(const Blk& b, int tile0, const int (&raw)[4],
-                                              int (&pg)[4], int (&rows)[4], int* bad)
+// That page and the number of its rows below the context; page -1 (and 0
+// rows) past the context or for an entry outside the pool (which also raises
+// *bad).
+__device__ __forceinline__ void resolve_page(const Blk& b, int key0, int raw, int& pg, int& rows,
+                                             int* bad)
 {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int key0 = tile0 + 16 * q;
-        const int p = __builtin_amdgcn_readfirstlane(raw[q]);
-        pg[q] = -1;
-        rows[q] = 0;
-        if (key0 < b.C) {
-            if (p < 0 || (int64_t)p >= b.n_pages) {
-                *bad = 1;
-            } else {
-                pg[q] = p;
-                rows[q] = min(16, b.C - key0);
-            }
+    const int p = __builtin_amdgcn_readfirstlane(raw);
+    pg = -1;
+    rows = 0;
+    if (key0 < b.C) {
+        if (p < 0 || (int64_t)p >= b.n_pages) {
+            *bad = 1;
+        } else {
+            pg = p;
+            rows = min(16, b.C - key0);
         }
     }
 }
 
-// bf16: every wave issues its share of the tile's 1 KiB blocks as buffer
-// loads that write LDS directly.
-template <int D>
-__device__ __forceinline__ void issue_direct(char* kbuf, char* vbuf, const Blk& b,
-                                             const uint8_t* kp, const uint8_t* vp, int tile0,
-                                             int wave, const int (&loff)[PGeo<D, false>::NBW],
-                                             const int (&raw)[4], int* bad)
+// bf16: this wave's KPW keys of one tensor's tile (one page), as buffer
+// loads that write LDS directly.  key0 is the page's first key.
+template <class G>
+__device__ __forceinline__ void issue_direct(char* dst, const uint8_t* pool, const Blk& b,
+                                             int key0, int wave, const int (&loff)[G::NBW],
+                                             int raw, int* bad)
 {
-    using G = PGeo<D, false>;
-    int pg[4], rows[4];
-    resolve_pages(b, tile0, raw, pg, rows, bad);
+    int pg, rows;
+    resolve_page(b, key0, raw, pg, rows, bad);
+    const int64_t base = ((int64_t)(pg < 0 ? 0 : pg) * b.Hk + b.kh) * 16 * G::ROWB;
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(pool + base), (short)0, rows * G::ROWB, kRsrcFlags);
 #pragma unroll
-    for (int i = 0; i < G::NBW; ++i) {
-        const int blk = wave * G::NBW + i;
-        const int q = (blk * G::RPB) >> 4;
-        const int64_t base = ((int64_t)(pg[q] < 0 ? 0 : pg[q]) * b.Hk + b.kh) * 16 * G::ROWB;
-        const int nrec = rows[q] * G::ROWB;
-        __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(kp + base), (short)0, nrec, kRsrcFlags);
-        __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(vp + base), (short)0, nrec, kRsrcFlags);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(kbuf + blk * 1024), 16, loff[i],
-                                                 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(vbuf + blk * 1024), 16, loff[i],
-                                                 0, 0, 0);
-    }
+    for (int i = 0; i < G::NBW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (LDS void*)(dst + (wave * G::NBW + i) * 1024), 16, loff[i], 0, 0, 0);
 }
 
-// fp8: a thread's share of the tile in registers between load and store.
-template <int D>
+// fp8: a lane's share of the wave's KPW keys of one tensor's tile in
+// registers between load and store, with the page's scale.
+template <class G>
 struct Staged {
-    u32x4 k[PGeo<D, true>::SCH];
-    u32x4 v[PGeo<D, true>::SCH];
-    float ks, vs;
+    u32x4 c[G::SCH];
+    float s;
 };
 
-template <int D>
-__device__ __forceinline__ void stage_load(Staged<D>& st, const Blk& b, const uint8_t* kp,
-                                           const uint8_t* vp, const float* ksc, const float* vsc,
-                                           int tile0, int tid, int* bad)
+template <class G>
+__device__ __forceinline__ void stage_load(Staged<G>& st, const uint8_t* pool, const float* scl,
+                                           const Blk& b, int key0, int wave, int lane, int raw,
+                                           int* bad)
 {
-    using G = PGeo<D, true>;
-    int pg[4], rows[4], raw[4];
-    fetch_pages(b, tile0, raw);
-    resolve_pages(b, tile0, raw, pg, rows, bad);
+    int pg, rows;
+    resolve_page(b, key0, raw, pg, rows, bad);
 #pragma unroll
     for (int i = 0; i < G::SCH; ++i) {
-        const int c = i * kThreads + tid;
-        const int key = c / G::CPR, piece = c % G::CPR;
-        const int q = key >> 4;
-        if ((key & 15) < rows[q]) {
+        const int c = i * 64 + lane;
+        const int pr = ((wave * G::KPW) & 15) + c / G::CPR, piece = c % G::CPR;  // page row
+        if (pr < rows) {
             const int64_t off =
-                (((int64_t)pg[q] * b.Hk + b.kh) * 16 + (key & 15)) * G::ROWB + piece * 16;
-            st.k[i] = *(const u32x4*)(kp + off);
-            st.v[i] = *(const u32x4*)(vp + off);
+                (((int64_t)pg * b.Hk + b.kh) * 16 + pr) * G::ROWB + piece * 16;
+            st.c[i] = *(const u32x4*)(pool + off);
         } else {
-            st.k[i] = u32x4{0u, 0u, 0u, 0u};
-            st.v[i] = u32x4{0u, 0u, 0u, 0u};
+            st.c[i] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    if (tid < 4) {  // pages past the context: scale 1 (their keys are masked)
-        st.ks = pg[tid] >= 0 ? ksc[(int64_t)pg[tid] * b.Hk + b.kh] : 1.f;
-        st.vs = pg[tid] >= 0 ? vsc[(int64_t)pg[tid] * b.Hk + b.kh] : 1.f;
-    }
+    // A page past the context gets scale 1 (its keys are masked).
+    if constexpr (G::EB == 1)
+        st.s = pg >= 0 ? scl[(int64_t)pg * b.Hk + b.kh] : 1.f;
+    else
+        st.s = 1.f;
 }
 
-template <int D>
-__device__ __forceinline__ void stage_store(const Staged<D>& st, char* kbuf, char* vbuf,
-                                            float* sc, int tid)
+template <class G>
+__device__ __forceinline__ void stage_store(const Staged<G>& st, char* buf, float* sc, int wave,
+                                            int lane)
 {
-    using G = PGeo<D, true>;
 #pragma unroll
     for (int i = 0; i < G::SCH; ++i) {
-        const int c = i * kThreads + tid;
-        const int key = c / G::CPR, piece = c % G::CPR;
-#pragma unroll
-        for (int kv = 0; kv < 2; ++kv) {
-            const u32x4 w = kv ? st.v[i] : st.k[i];
-            char* row = (kv ? vbuf : kbuf) + key * G::ROWL;
-            u32x4 lo, hi;
-            lo[0] = fp8x2_to_bf16x2<false>(w[0]);
-            lo[1] = fp8x2_to_bf16x2<true>(w[0]);
-            lo[2] = fp8x2_to_bf16x2<false>(w[1]);
-            lo[3] = fp8x2_to_bf16x2<true>(w[1]);
-            hi[0] = fp8x2_to_bf16x2<false>(w[2]);
-            hi[1] = fp8x2_to_bf16x2<true>(w[2]);
-            hi[2] = fp8x2_to_bf16x2<false>(w[3]);
-            hi[3] = fp8x2_to_bf16x2<true>(w[3]);
-            *(u32x4*)(row + ((2 * piece) ^ swz(key)) * 16) = lo;
-            *(u32x4*)(row + ((2 * piece + 1) ^ swz(key)) * 16) = hi;
+        const int c = i * 64 + lane;
+        const int key = wave * G::KPW + c / G::CPR, piece = c % G::CPR;
+        const u32x4 w = st.c[i];
+        char* row = buf + key * G::ROWL;
+        if constexpr (G::EB == 2) {  // bf16: stored as loaded
+            *(u32x4*)(row + (piece ^ swz(key)) * 16) = w;
+            continue;
         }
+        u32x4 lo, hi;
+        lo[0] = fp8x2_to_bf16x2<false>(w[0]);
+        lo[1] = fp8x2_to_bf16x2<true>(w[0]);
+        lo[2] = fp8x2_to_bf16x2<false>(w[1]);
+        lo[3] = fp8x2_to_bf16x2<true>(w[1]);
+        hi[0] = fp8x2_to_bf16x2<false>(w[2]);
+        hi[1] = fp8x2_to_bf16x2<true>(w[2]);
+        hi[2] = fp8x2_to_bf16x2<false>(w[3]);
+        hi[3] = fp8x2_to_bf16x2<true>(w[3]);
+        *(u32x4*)(row + ((2 * piece) ^ swz(key)) * 16) = lo;
+        *(u32x4*)(row + ((2 * piece + 1) ^ swz(key)) * 16) = hi;
     }
-    if (tid < 4) {
-        sc[tid] = st.ks;
-        sc[4 + tid] = st.vs;
-    }
+    if (lane == 0 && ((wave * G::KPW) & 15) == 0)
+        sc[(wave * G::KPW) >> 4] = st.s;
 }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
+// Max over the 4 lanes n, n + 16, n + 32, n + 48 (the lanes of one row).
+__device__ __forceinline__ float row_max4(float v)
 {
-    using G = PGeo<D, FP8>;
-    __shared__ __attribute__((aligned(1024))) char smem0[G::BUF];
-    __shared__ __attribute__((aligned(1024))) char smem1[G::BUF];
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+__device__ __forceinline__ float row_sum4(float v)
+{
+    v = v + __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+template <int D, bool FP8, int RT, int NW>
+__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(PrefillArgs a)
+{
+    using G = PGeo<D, FP8, RT, NW>;
+    constexpr bool STG = FP8;  // staged through registers (fp8) or LDS-direct (bf16)
+    __shared__ __attribute__((aligned(1024))) char s_k0[G::TILEB];
+    __shared__ __attribute__((aligned(1024))) char s_k1[G::TILEB];
+    __shared__ __attribute__((aligned(1024))) char s_v0[G::TILEB];
+    __shared__ __attribute__((aligned(1024))) char s_v1[G::TILEB];
+    __shared__ float s_ksc[2][4], s_vsc[2][4];  // fp8 page scales of each buffer
     __shared__ int s_bad;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 15, kb = lane >> 4;
-    const int Hk = a.n_head_kv, H = a.n_head, g = H / Hk, BP = 128 / g;
+    const int Hk = a.n_head_kv, H = a.n_head, g = H / Hk, BP = G::ROWS / g;
     const int npb = (a.n_rows + BP - 1) / BP;
     const int nblk = npb * Hk;
     // XCD-aware placement: consecutive list entries (same kv head) go to the
@@ -277,33 +275,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     b.n_pages = a.n_pages;
     b.bt = a.block_table;
     const int base_pos = a.ctx_len - a.n_rows;
-
-    // This lane's query row (row n of the wave's 16).
-    const int wrow = 16 * wave + n;            // 0..127 in the workgroup
-    const int hg = wrow / BP, p = wrow - hg * BP;
-    const int r = pb * BP + p;                 // row of the call
-    const bool valid = r < a.n_rows;
-    const int h = kh * g + hg;
-    const int pos = valid ? base_pos + r : -1;
     const int rlast = min(a.n_rows, (pb + 1) * BP) - 1;
-    const int maxpos = base_pos + rlast;       // last key any row here needs
+    const int maxpos = base_pos + rlast;  // last key any row here needs
     const int minpos = base_pos + pb * BP;
     const int nt = (maxpos + kKT) / kKT;
 
-    // Q^T operand: 8 bf16 of the lane's row per k-step (d = 32 st + 8 kb + i).
-    u32x4 qop[G::KSTEPS];
-    {
-        const uint16_t* q = (const uint16_t*)a.q + ((int64_t)(valid ? r : 0) * H + h) * D;
+    // The lane's query row in each of the wave's row tiles (row n of 16).
+    int row[RT], head[RT], pos[RT];
+    u32x4 qop[RT][G::KSTEPS];  // Q^T operand: d = 32 st + 8 kb + 0..7
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int wrow = 16 * (RT * wave + rt) + n;  // row in the workgroup
+        const int hg = wrow / BP, p = wrow - hg * BP;
+        row[rt] = pb * BP + p;
+        head[rt] = kh * g + hg;
+        const bool valid = row[rt] < a.n_rows;
+        pos[rt] = valid ? base_pos + row[rt] : -1;
+        const uint16_t* q =
+            (const uint16_t*)a.q + ((int64_t)(valid ? row[rt] : 0) * H + head[rt]) * D;
 #pragma unroll
         for (int st = 0; st < G::KSTEPS; ++st)
-            qop[st] = valid ? *(const u32x4*)(q + 32 * st + 8 * kb) : u32x4{0u, 0u, 0u, 0u};
+            qop[rt][st] = valid ? *(const u32x4*)(q + 32 * st + 8 * kb) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    f32x4 O[G::DBLK];
+    f32x4 O[RT][G::DBLK];
+    float m[RT], l[RT];  // l: this lane's part of the row sum
 #pragma unroll
-    for (int jb = 0; jb < G::DBLK; ++jb)
-        O[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = neg_inf(), l = 0.f;
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int jb = 0; jb < G::DBLK; ++jb)
+            O[rt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[rt] = neg_inf();
+        l[rt] = 0.f;
+    }
     const float sm_log2 = kLog2e / __builtin_sqrtf((float)D);
 
     if (tid == 0)
@@ -321,8 +325,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
         const int rr = lane / G::CPRL, pc = lane % G::CPRL;
 #pragma unroll
         for (int i = 0; i < G::NBW; ++i) {
-            const int row = (wave * G::NBW + i) * G::RPB + rr;
-            loff[i] = (row & 15) * G::ROWB + ((pc ^ swz(row)) * 16);
+            const int r = (wave * G::NBW + i) * G::RPB + rr;
+            loff[i] = (r & 15) * G::ROWB + ((pc ^ swz(r)) * 16);
         }
     }
     // K reads: key row 16 kq + n (kq = 16-key block), logical chunk 4 st + kb.
@@ -347,122 +351,185 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             voff[j] = vkey * G::ROWL + 16 * ((2 * j + ((n & 3) >> 1)) ^ sw) + (n & 1) * 8;
     }
 
-    Staged<D> stg;
-    int rawn[4];  // block-table entries of the next tile to load
-    char* buf0 = smem0;
-    if constexpr (FP8) {
-        stage_load<D>(stg, b, kp, vp, a.k_scale, a.v_scale, 0, tid, &bad);
-        stage_store<D>(stg, buf0, buf0 + G::TILEB, (float*)(buf0 + 2 * G::TILEB), tid);
-    } else {
-        int raw0[4];
-        fetch_pages(b, 0, raw0);
-        issue_direct<D>(buf0, buf0 + G::TILEB, b, kp, vp, 0, wave, loff, raw0, &bad);
-        fetch_pages(b, kKT, rawn);
-        __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();
+    // S^T of a tile: [row tile][16-key block]; two sets, current and next.
+    f32x4 sa[RT][4], sb[RT][4];
+    float ka[4], kb4[4];  // K page scales (fp8) of the tile in sa / sb
+    auto scores = [&](const char* ks, f32x4 (&acc)[RT][4], int kq) {
+        u32x4 kw[G::KSTEPS];
+#pragma unroll
+        for (int st = 0; st < G::KSTEPS; ++st)
+            kw[st] = *(const u32x4*)(ks + koff[st % KBS] + kq * 16 * G::ROWL + 256 * (st / KBS));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            acc[rt][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < G::KSTEPS; ++st)
+                acc[rt][kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, kw[st]), __builtin_bit_cast(bf16x8, qop[rt][st]),
+                    acc[rt][kq], 0, 0, 0);
+        }
+    };
 
-    auto tile_body = [&](int t, char* cbuf, char* nbuf) {
+    // The wave loads keys wave * KPW .. + KPW - 1 of every tile: one page,
+    // whose first key is tile0 + wk.
+    const int wk = ((wave * G::KPW) >> 4) * 16;
+    Staged<G> stk, stv;
+    int rawv = fetch_page(b, wk);        // block-table entries of the next V
+    int rawk = fetch_page(b, kKT + wk);  // and K tiles to load
+    if constexpr (STG) {
+        stage_load<G>(stk, kp, a.k_scale, b, wk, wave, lane, rawv, &bad);
+        stage_store<G>(stk, s_k0, s_ksc[0], wave, lane);
+        stage_load<G>(stv, vp, a.v_scale, b, wk, wave, lane, rawv, &bad);
+        stage_store<G>(stv, s_v0, s_vsc[0], wave, lane);
+        if (nt > 1) {
+            stage_load<G>(stk, kp, a.k_scale, b, kKT + wk, wave, lane, rawk, &bad);
+            stage_store<G>(stk, s_k1, s_ksc[1], wave, lane);
+        }
+    } else {
+        issue_direct<G>(s_k0, kp, b, wk, wave, loff, rawv, &bad);
+        issue_direct<G>(s_v0, vp, b, wk, wave, loff, rawv, &bad);
+        if (nt > 1)
+            issue_direct<G>(s_k1, kp, b, kKT + wk, wave, loff, rawk, &bad);
+    }
+    rawv = rawk;
+    rawk = fetch_page(b, 2 * kKT + wk);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+        scores(s_k0, sa, kq);
+        ka[kq] = FP8 ? s_ksc[0][kq] : 1.f;
+    }
+
+    // Iteration t: K(t+1) in kr, V(t) in vr; fills K(t+2) into kw and V(t+1)
+    // into vw.  cur holds S^T(t) (kc its K scales); nxt receives S^T(t+1).
+    auto tile_body = [&](int t, const char* kr, const char* vr, char* kwb, char* vwb,
+                         const float* krs, const float* vrs, float* kws, float* vws,
+                         f32x4 (&cur)[RT][4], const float (&kc)[4], f32x4 (&nxt)[RT][4],
+                         float (&kn)[4]) {
         const int tile0 = t * kKT;
         if (t + 1 < nt) {
-            if constexpr (FP8)
-                stage_load<D>(stg, b, kp, vp, a.k_scale, a.v_scale, tile0 + kKT, tid, &bad);
-            else {
-                issue_direct<D>(nbuf, nbuf + G::TILEB, b, kp, vp, tile0 + kKT, wave, loff, rawn,
-                                &bad);
-                fetch_pages(b, tile0 + 2 * kKT, rawn);
+            if constexpr (STG)
+                stage_load<G>(stv, vp, a.v_scale, b, tile0 + kKT + wk, wave, lane, rawv, &bad);
+            else
+                issue_direct<G>(vwb, vp, b, tile0 + kKT + wk, wave, loff, rawv, &bad);
+        }
+        if (t + 2 < nt) {
+            if constexpr (STG)
+                stage_load<G>(stk, kp, a.k_scale, b, tile0 + 2 * kKT + wk, wave, lane, rawk,
+                              &bad);
+            else
+                issue_direct<G>(kwb, kp, b, tile0 + 2 * kKT + wk, wave, loff, rawk, &bad);
+        }
+        rawv = rawk;
+        rawk = fetch_page(b, tile0 + 3 * kKT + wk);
+
+        // Scale (log2 units) and, on the tile that crosses the causal edge,
+        // mask; then the lane-local max check.
+        const bool diag = tile0 + kKT - 1 > minpos;
+        float sx[4];  // factor applied to cur in the exponent
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+            sx[kq] = FP8 ? kc[kq] * sm_log2 : sm_log2;
+        float lmax[RT];
+        if (diag) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float mx = neg_inf();
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float v = tile0 + 16 * kq + 4 * kb + x > pos[rt]
+                                            ? neg_inf()
+                                            : cur[rt][kq][x] * sx[kq];
+                        cur[rt][kq][x] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                lmax[rt] = mx;
+            }
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+                sx[kq] = 1.f;
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float mx = neg_inf();
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const float bm = fmaxf(fmaxf(cur[rt][kq][0], cur[rt][kq][1]),
+                                           fmaxf(cur[rt][kq][2], cur[rt][kq][3]));
+                    mx = FP8 ? fmaxf(mx, bm * sx[kq]) : fmaxf(mx, bm);
+                }
+                lmax[rt] = FP8 ? mx : mx * sm_log2;
             }
         }
-        const char* buf = cbuf;
-        const char* ks = buf;
-        const char* vs = buf + G::TILEB;
-        const float* sc = (const float*)(buf + 2 * G::TILEB);
-        const bool diag = tile0 + kKT - 1 > minpos;  // the causal edge crosses this tile
-
-        // Two 32-key halves; per half: S^T (2 key blocks), a rescale check
-        // (rarely taken), exp/sum/pack, PV (one 32-key k-step per d block).
-        f32x4 acc[4];
-        u32x4 pb2[2];  // P^T operands of the two 32-key k-steps
-        // Operands of a 16-key block are read from LDS in one batch before its
-        // MFMAs, so the reads' latency overlaps instead of gating each MFMA.
-        auto s_half = [&](int hf) {
+        bool up = false;
 #pragma unroll
-            for (int kq = 2 * hf; kq < 2 * hf + 2; ++kq) {
-                u32x4 kw[G::KSTEPS];
+        for (int rt = 0; rt < RT; ++rt)
+            up = up || lmax[rt] > m[rt] + kTau;
+        if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
-                for (int st = 0; st < G::KSTEPS; ++st)
-                    kw[st] = *(const u32x4*)(ks + koff[st % KBS] + kq * 16 * G::ROWL +
-                                             256 * (st / KBS));
-                acc[kq] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < G::KSTEPS; ++st)
-                    acc[kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, kw[st]), __builtin_bit_cast(bf16x8, qop[st]),
-                        acc[kq], 0, 0, 0);
-            }
-        };
-        // One max check over the whole tile, before any of its scores is
-        // turned into a probability: a rescale between the two halves would
-        // leave the first half's P relative to the old max.
-        auto check_tile = [&]() {
-            float tmax = neg_inf();
-#pragma unroll
-            for (int kq = 0; kq < 4; ++kq) {
-                const float s = FP8 ? sc[kq] * sm_log2 : sm_log2;
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    float v = acc[kq][x] * s;
-                    if (diag && tile0 + 16 * kq + 4 * kb + x > pos)
-                        v = neg_inf();
-                    acc[kq][x] = v;
-                    tmax = fmaxf(tmax, v);
-                }
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            if (__builtin_amdgcn_ballot_w64(tmax > m + kTau)) {
-                const float mnew = fmaxf(m, tmax);
+            for (int rt = 0; rt < RT; ++rt) {
+                const float mnew = fmaxf(m[rt], row_max4(lmax[rt]));
                 const float alpha =
-                    m == neg_inf() ? 0.f : (m == mnew ? 1.f : __builtin_amdgcn_exp2f(m - mnew));
-                l = l * alpha;
+                    m[rt] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mnew);
+                l[rt] = l[rt] * alpha;
 #pragma unroll
                 for (int jb = 0; jb < G::DBLK; ++jb)
-                    O[jb] = O[jb] * alpha;
-                m = mnew;
+                    O[rt][jb] = O[rt][jb] * alpha;
+                m[rt] = mnew;
             }
-        };
-        auto softmax_half = [&](int hf) {
-            const float muse = m == neg_inf() ? 0.f : m;
-            float e[2][4];
-            float psum = 0.f;
+        }
+
+        // Scores of tile t+1 (on stale K past the last tile: never used),
+        // interleaved with tile t's probabilities.
+        float muse[RT];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int kq = 2 * hf + j;
-                const float vscale = FP8 ? sc[4 + kq] : 1.f;
+        for (int rt = 0; rt < RT; ++rt)
+            muse[rt] = m[rt] == neg_inf() ? 0.f : m[rt];
+        float e[RT][4][4];
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            scores(kr, nxt, kq);
+            kn[kq] = FP8 ? krs[kq] : 1.f;
+            const float vsc = FP8 ? vrs[kq] : 1.f;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float pe[4];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    const float pe = __builtin_amdgcn_exp2f(acc[kq][x] - muse);
-                    psum = psum + pe;
-                    e[j][x] = FP8 ? pe * vscale : pe;
+                    pe[x] =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(cur[rt][kq][x], sx[kq], -muse[rt]));
+                    e[rt][kq][x] = FP8 ? pe[x] * vsc : pe[x];
                 }
+                l[rt] = l[rt] + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
             }
-            pb2[hf][0] = pack_bf16(e[0][0], e[0][1]);
-            pb2[hf][1] = pack_bf16(e[0][2], e[0][3]);
-            pb2[hf][2] = pack_bf16(e[1][0], e[1][1]);
-            pb2[hf][3] = pack_bf16(e[1][2], e[1][3]);
-            psum = psum + __shfl_xor(psum, 16, 64);
-            psum = psum + __shfl_xor(psum, 32, 64);
-            l = l + psum;
-        };
-        auto pv_half = [&](int hf) {
-            constexpr int NB = 8;  // d blocks per batch of V reads
+        }
+        // P^T operands: k index i of the 32-key half hf is key
+        // 32 hf + 16 (i / 4) + 4 kb + i % 4, matching the V^T reads.
+        u32x4 pb[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                pb[rt][hf][0] = pack_bf16(e[rt][2 * hf][0], e[rt][2 * hf][1]);
+                pb[rt][hf][1] = pack_bf16(e[rt][2 * hf][2], e[rt][2 * hf][3]);
+                pb[rt][hf][2] = pack_bf16(e[rt][2 * hf + 1][0], e[rt][2 * hf + 1][1]);
+                pb[rt][hf][3] = pack_bf16(e[rt][2 * hf + 1][2], e[rt][2 * hf + 1][3]);
+            }
+
+        // O^T += V^T . P^T, one 32-key k-step per half and d block.
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            constexpr int NB = 4;  // d blocks per batch of V reads
 #pragma unroll
             for (int j0 = 0; j0 < G::DBLK; j0 += NB) {
                 u32x4 va[NB];
 #pragma unroll
                 for (int jj = 0; jj < NB; ++jj) {
                     const int jb = j0 + jj;
-                    const char* v0 = vs + voff[jb % VBS] + 32 * hf * G::ROWL + 256 * (jb / VBS);
+                    const char* v0 = vr + voff[jb % VBS] + 32 * hf * G::ROWL + 256 * (jb / VBS);
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)v0);
                     const s16x4 hi =
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(v0 + 16 * G::ROWL));
@@ -472,62 +539,65 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
                 }
 #pragma unroll
                 for (int jj = 0; jj < NB; ++jj)
-                    O[j0 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, va[jj]), __builtin_bit_cast(bf16x8, pb2[hf]),
-                        O[j0 + jj], 0, 0, 0);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        O[rt][j0 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, va[jj]),
+                            __builtin_bit_cast(bf16x8, pb[rt][hf]), O[rt][j0 + jj], 0, 0, 0);
             }
-        };
-        s_half(0);
-        s_half(1);
-        check_tile();
-        softmax_half(0);
-        pv_half(0);
-        softmax_half(1);
-        pv_half(1);
+        }
 
-        if (t + 1 < nt) {
-            if constexpr (FP8)
-                stage_store<D>(stg, nbuf, nbuf + G::TILEB, (float*)(nbuf + 2 * G::TILEB), tid);
-            else
-                __builtin_amdgcn_s_waitcnt(0);
+        if constexpr (STG) {
+            if (t + 1 < nt)
+                stage_store<G>(stv, vwb, vws, wave, lane);
+            if (t + 2 < nt)
+                stage_store<G>(stk, kwb, kws, wave, lane);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
         }
         __syncthreads();
     };
     for (int t = 0; t < nt; t += 2) {
-        tile_body(t, smem0, smem1);
+        tile_body(t, s_k1, s_v0, s_k0, s_v1, s_ksc[1], s_vsc[0], s_ksc[0], s_vsc[1], sa, ka, sb,
+                  kb4);
         if (t + 1 < nt)
-            tile_body(t + 1, smem1, smem0);
+            tile_body(t + 1, s_k0, s_v1, s_k1, s_v0, s_ksc[0], s_vsc[1], s_ksc[1], s_vsc[0], sb,
+                      kb4, sa, ka);
     }
 
     if (bad)
         s_bad = 1;
     __syncthreads();
-    if (!valid)
-        return;
     const bool nan = s_bad != 0;
-    const float inv = 1.f / l;
-    uint16_t* out = (uint16_t*)a.out + ((int64_t)r * H + h) * D;
 #pragma unroll
-    for (int jb = 0; jb < G::DBLK; ++jb) {
-        const int d = 16 * jb + 4 * kb;
-        u32x2 o;
-        o[0] = nan ? 0x7FC07FC0u : pack_bf16(O[jb][0] * inv, O[jb][1] * inv);
-        o[1] = nan ? 0x7FC07FC0u : pack_bf16(O[jb][2] * inv, O[jb][3] * inv);
-        *(u32x2*)(out + d) = o;
+    for (int rt = 0; rt < RT; ++rt) {
+        const float inv = 1.f / row_sum4(l[rt]);
+        if (row[rt] >= a.n_rows)
+            continue;
+        uint16_t* out = (uint16_t*)a.out + ((int64_t)row[rt] * H + head[rt]) * D;
+#pragma unroll
+        for (int jb = 0; jb < G::DBLK; ++jb) {
+            const int d = 16 * jb + 4 * kb;
+            u32x2 o;
+            o[0] = nan ? 0x7FC07FC0u : pack_bf16(O[rt][jb][0] * inv, O[rt][jb][1] * inv);
+            o[1] = nan ? 0x7FC07FC0u : pack_bf16(O[rt][jb][2] * inv, O[rt][jb][3] * inv);
+            *(u32x2*)(out + d) = o;
+        }
     }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int RT, int NW>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream)
 {
+    using G = PGeo<D, FP8, RT, NW>;
     const int g = a.n_head / a.n_head_kv;
-    const int BP = 128 / g;
+    const int BP = G::ROWS / g;
     const int npb = (a.n_rows + BP - 1) / BP;
     const int nblk = npb * a.n_head_kv;
     const int grid = ((nblk + 7) / 8) * 8;
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, stream);
-    hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, RT, NW>), dim3(grid), dim3(G::NTH), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_stop)
         (void)hipEventRecord(a.ev_stop, stream);
@@ -541,10 +611,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
     const int g = a.n_head / a.n_head_kv;
     if (g > 128 || 128 % g != 0)
         return hipErrorNotSupported;
+    // One 16-row tile per wave, eight waves: two waves per SIMD, so one
+    // wave's softmax overlaps the other's matrix work.  (Two row tiles per
+    // wave halve the LDS reads per flop but need more than the 256 VGPRs of
+    // a wave at this occupancy for head_dim 256.)
     if (a.head_dim == 128)
-        return a.fp8 ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+        return a.fp8 ? launch_t<128, true, 1, 8>(a, stream) : launch_t<128, false, 1, 8>(a, stream);
     if (a.head_dim == 256)
-        return a.fp8 ? launch_t<256, true>(a, stream) : launch_t<256, false>(a, stream);
+        return a.fp8 ? launch_t<256, true, 1, 8>(a, stream) : launch_t<256, false, 1, 8>(a, stream);
     return hipErrorNotSupported;
 }
 
