@@ -108,12 +108,16 @@ def prefill_flops(n_rows, ctx, w):
     return 4 * w.n_head * w.head_dim * pairs
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in ("decode.hip", "prefill.hip", "append.hip"):
-        with open(os.path.join(ROOT, "paged_kv_cache_20_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+# The source file each profiled kernel is built from.
+KERNEL_SOURCE = {"split_kernel": "decode.hip", "combine_kernel": "decode.hip",
+                 "prefill_kernel": "prefill.hip"}
+
+
+def kernel_source_hash(kernel_key):
+    """First 16 hex digits of the sha256 of the kernel's source file."""
+    src = KERNEL_SOURCE[kernel_key.split("_decode")[0].split("_prefill")[0]]
+    with open(os.path.join(ROOT, "paged_kv_cache_20_amd", "csrc", src), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel_key):
@@ -126,7 +130,7 @@ def traffic_from_profiles(kernel_key):
     except (OSError, ValueError):
         return None
     e = d.get(kernel_key)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel_key):
         return None
     return e.get("bytes_per_launch")
 
