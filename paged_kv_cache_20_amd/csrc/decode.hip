@@ -389,23 +389,31 @@ struct Item {
     int s, j, kh, C, t0, t1, npg;
 };
 
-__device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_len, int S, int Hk,
-                                             int item)
+// Items are numbered full splits first (sequence, split, kv head), then the
+// partial last splits (sequence, kv head): a wave's later items are the
+// short ones, so the grid's last round is short.  s_pre / s_pp: exclusive
+// prefixes over sequences of their full / partial items.
+__device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, const int* s_len,
+                                             int S, int Hk, int item)
 {
+    const int nfull = s_pre[S];
+    const bool full = item < nfull;
+    const int* pre = full ? s_pre : s_pp;
+    const int key = full ? item : item - nfull;
     int lo = 0, hi = S - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= item)
+        if (pre[mid] <= key)
             lo = mid;
         else
             hi = mid - 1;
     }
     Item it;
     it.s = __builtin_amdgcn_readfirstlane(lo);
-    const int local = __builtin_amdgcn_readfirstlane(item - s_pre[it.s]);
-    it.j = local / Hk;
-    it.kh = local - it.j * Hk;
+    const int local = __builtin_amdgcn_readfirstlane(key - pre[it.s]);
     it.C = __builtin_amdgcn_readfirstlane(s_len[it.s]);
+    it.j = full ? local / Hk : it.C / kChunk;
+    it.kh = full ? local - it.j * Hk : local;
     it.t0 = it.j * kChunk;
     it.t1 = min(it.t0 + kChunk, it.C);
     it.npg = (it.t1 - it.t0 + 15) >> 4;
@@ -429,55 +437,67 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     constexpr int NBUF = Plan<D, FP8, NT>::NBUF;
     constexpr bool PREQ = Plan<D, FP8, NT>::PREQ;
     constexpr int KT = G::KT;
-    __shared__ int s_pre[kMaxSeq + 1];
+    __shared__ int s_pre[kMaxSeq + 1];  // full items before each sequence
+    __shared__ int s_pp[kMaxSeq + 1];   // partial items before each sequence
     __shared__ int s_len[kMaxSeq];
-    __shared__ int s_tmp[256];
+    __shared__ int s_tmp[256], s_tmp2[256];
 
     const int S = a.n_seq, R = a.rows, Hk = a.n_head_kv, H = a.n_head;
     const int g = H / Hk, ppt = 16 / g;
     const int64_t cap = (int64_t)a.max_pages * 16;
     const int tid = threadIdx.x;
 
-    // Exclusive prefix over sequences of their work items, and the lengths
-    // (kept in LDS: item set-up then waits on no global load).
+    // Exclusive prefixes over sequences of their full and partial work items,
+    // and the lengths (kept in LDS: item set-up then waits on no global load).
     {
+        auto nfull = [&](int C) { return ctx_ok(C, R, cap) ? (C / kChunk) * Hk : 0; };
+        auto npart = [&](int C) { return ctx_ok(C, R, cap) && C % kChunk != 0 ? Hk : 0; };
         const int per = (S + 255) / 256;
         const int b0 = tid * per;
-        int loc = 0;
+        int loc = 0, loc2 = 0;
         for (int i = 0; i < per; ++i) {
             const int s = b0 + i;
             if (s < S) {
                 const int C = a.ctx_lens[s];
-                loc += ctx_ok(C, R, cap) ? ((C + kChunk - 1) / kChunk) * Hk : 0;
+                loc += nfull(C);
+                loc2 += npart(C);
             }
         }
         s_tmp[tid] = loc;
+        s_tmp2[tid] = loc2;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
             const int v = tid >= off ? s_tmp[tid - off] : 0;
+            const int v2 = tid >= off ? s_tmp2[tid - off] : 0;
             __syncthreads();
             s_tmp[tid] += v;
+            s_tmp2[tid] += v2;
             __syncthreads();
         }
         int run = tid ? s_tmp[tid - 1] : 0;
+        int run2 = tid ? s_tmp2[tid - 1] : 0;
         for (int i = 0; i < per; ++i) {
             const int s = b0 + i;
             if (s < S) {
                 s_pre[s] = run;
+                s_pp[s] = run2;
                 const int C = a.ctx_lens[s];
                 s_len[s] = C;
-                run += ctx_ok(C, R, cap) ? ((C + kChunk - 1) / kChunk) * Hk : 0;
+                run += nfull(C);
+                run2 += npart(C);
             }
         }
-        if (tid == 255)
+        if (tid == 255) {
             s_pre[S] = s_tmp[255];
+            s_pp[S] = s_tmp2[255];
+        }
         __syncthreads();
     }
 
     const int lane = tid & 63, n = lane & 15, kb = lane >> 4;
     // Wave-uniform values are made visibly uniform (scalar registers), so
     // that loop bounds, page ids and buffer resources stay scalar.
-    const int total = __builtin_amdgcn_readfirstlane(s_pre[S]);
+    const int total = __builtin_amdgcn_readfirstlane(s_pre[S] + s_pp[S]);
     const int nwaves = gridDim.x * kWaves;
     const float sm_log2 = kLog2e / __builtin_sqrtf((float)D);
     const uint8_t* __restrict__ kp = (const uint8_t*)a.k_pool;
@@ -548,10 +568,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     // are not computed), so every item starts at ring slot 0.
     // Table entries are fetched two items ahead and held in registers one
     // item ahead, so the ring never waits for them.
-    Item cur = resolve_item(s_pre, s_len, S, Hk, item);
+    Item cur = resolve_item(s_pre, s_pp, s_len, S, Hk, item);
     int pid = fetch_pages(a, cur, true);
     bool has_next = item + nwaves < total;
-    Item nxt = resolve_item(s_pre, s_len, S, Hk, has_next ? item + nwaves : item);
+    Item nxt = resolve_item(s_pre, s_pp, s_len, S, Hk, has_next ? item + nwaves : item);
     int pid_n = fetch_pages(a, nxt, has_next);
     // A full wait (never too weak): the loop then finds pid and pid_n
     // resolved on entry as it does on every later iteration, and its
@@ -570,7 +590,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         // The item after next: geometry and table entries now.
         const int next2 = item + 2 * nwaves;
         const bool has_next2 = next2 < total;
-        const Item nxt2 = resolve_item(s_pre, s_len, S, Hk, has_next2 ? next2 : item);
+        const Item nxt2 = resolve_item(s_pre, s_pp, s_len, S, Hk, has_next2 ? next2 : item);
         const int pid_nn = fetch_pages(a, nxt2, has_next2);
 
         const int s = cur.s, j = cur.j, kh = cur.kh, C = cur.C, t0 = cur.t0, t1 = cur.t1;
