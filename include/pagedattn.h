@@ -177,6 +177,43 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_paged_mixed -- a continuous-batching step: decode rows of
+ * n_seq_decode sequences beside prefill chunks of the other sequences, in
+ * one call ("Radiance Architecture Plugins -- declaring a model", section
+ * "Step: issuing the graph": the core orders a mixed step decode-first, the
+ * decode path runs over the first n_seq_decode sequences and the chunked
+ * path over the rest, whose token offsets in cu_seqlens are absolute).
+ *
+ *   q, out       bf16 [n_tok][n_head][head_dim], token rows in step order
+ *   cu_seqlens   int32 [n_seq + 1], DEVICE: sequence s owns token rows
+ *                cu_seqlens[s] .. cu_seqlens[s + 1] - 1.  Decode-first:
+ *                sequence s < n_seq_decode owns exactly row s.  Only the
+ *                entries from n_seq_decode on are read (NULL allowed when
+ *                n_seq_decode == n_seq).
+ *   block_table  int32 [n_seq][max_pages_per_seq]
+ *   ctx_lens     int32 [n_seq], DEVICE: lengths after this call
+ *   max_q_len    HOST bound on the rows of any chunk (sizes the grid); the
+ *                chunks' own row counts stay on the device
+ *   workspace    attn_paged_workspace_bytes(3, n_seq_decode, ...)
+ * Each decode row is bit for bit what attn_paged_decode returns for its
+ * sequence, and each chunk row what attn_paged_prefill returns for its
+ * chunk: the two halves run the same kernels on the same stream.  Host
+ * checks: n_tok >= 1, 0 <= n_seq_decode <= n_seq, a chunk half needs
+ * cu_seqlens, 1 <= max_q_len <= n_tok - n_seq_decode, and a decode-only step
+ * has n_tok == n_seq.  On the device, a chunk whose rows fall outside
+ * 1 .. max_q_len or past n_tok, or whose ctx_len is below its rows or
+ * beyond the block-table row, is skipped (its rows of out are not written);
+ * decode sequences follow the rules of attn_paged_decode.
+ */
+int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, int32_t n_seq,
+                     int32_t n_seq_decode, int32_t max_q_len, const void* k_pool,
+                     const void* v_pool, const float* k_scale, const float* v_scale,
+                     int64_t n_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                     const int32_t* ctx_lens, int32_t n_head, int32_t n_head_kv,
+                     int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype, void* out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_kv_append -- write n_tok new K/V rows into their token slots
  * ("kern manifest v7" schema, $defs.Fill "slot": each row's token slot in
  * the paged state; slot = page * page_size + offset).  A negative slot skips
@@ -217,8 +254,9 @@ int attn_block_table_build(int32_t n_seq, const int32_t* ctx_lens_host, int32_t 
                            int64_t pool_pages, uint64_t seed, int32_t max_pages_per_seq,
                            int32_t* block_table_host, int32_t* slot_mapping_host);
 
-/* op: 0 decode, 1 verify, 2 prefill.  Bytes of device workspace the call
-   needs; 0 for an unsupported combination. */
+/* op: 0 decode, 1 verify, 2 prefill, 3 mixed (n_seq = the step's
+   n_seq_decode).  Bytes of device workspace the call needs; 0 for an
+   unsupported combination. */
 size_t attn_paged_workspace_bytes(int op, int32_t n_seq, int32_t max_pages_per_seq,
                                   int32_t n_head, int32_t head_dim);
 
@@ -242,7 +280,8 @@ const char* attn_last_error(void);
 /*
  * Measurement hook: the next decode, verify or prefill call made on this
  * thread records `start` just before and `stop` just after its main
- * attention kernel, on the call's stream, then forgets both.  Pass NULLs to
+ * attention kernel (a mixed call: around both of its halves), on the call's
+ * stream, then forgets both.  Pass NULLs to
  * cancel.  Lets a benchmark time that kernel alone with HIP events.
  */
 void attn_set_kernel_timer(hipEvent_t start, hipEvent_t stop);

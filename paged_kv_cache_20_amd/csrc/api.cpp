@@ -227,6 +227,7 @@ size_t attn_paged_workspace_bytes(int op, int32_t n_seq, int32_t max_pages_per_s
     case 0: return split_ws_bytes(1, n_seq, max_pages_per_seq, n_head, head_dim);
     case 1: return split_ws_bytes(ATTN_VERIFY_ROWS, n_seq, max_pages_per_seq, n_head, head_dim);
     case 2: return 0;
+    case 3: return split_ws_bytes(1, n_seq, max_pages_per_seq, n_head, head_dim);
     default: return 0;
     }
 }
@@ -299,7 +300,101 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
     a.ev_start = t_ev_start;
     a.ev_stop = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
+    a.cu_seqlens = nullptr;
+    a.ctx_lens = nullptr;
+    a.n_var = 1;
+    a.max_q_len = n_rows;
+    a.n_tok = n_rows;
     return from_hip(pa::launch_prefill(a, stream), fn);
+}
+
+int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, int32_t n_seq,
+                     int32_t n_seq_decode, int32_t max_q_len, const void* k_pool,
+                     const void* v_pool, const float* k_scale, const float* v_scale,
+                     int64_t n_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                     const int32_t* ctx_lens, int32_t n_head, int32_t n_head_kv,
+                     int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype, void* out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char* fn = "attn_paged_mixed";
+    int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                          max_pages_per_seq, n_head, n_head_kv, head_dim, page_size, kv_dtype,
+                          out);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!ctx_lens)
+        return fail(ATTN_E_ARG, "%s: ctx_lens is NULL", fn);
+    if (n_tok <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (n_tok = %d)", fn, n_tok);
+    if (n_seq <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero sequences is not a call (n_seq = %d)", fn, n_seq);
+    if (n_seq_decode < 0 || n_seq_decode > n_seq)
+        return fail(ATTN_E_SHAPE, "%s: n_seq_decode %d outside 0 .. n_seq (%d)", fn,
+                    n_seq_decode, n_seq);
+    const int32_t n_chunk = n_seq - n_seq_decode;
+    if (n_chunk > 0) {
+        if (!cu_seqlens)
+            return fail(ATTN_E_ARG, "%s: cu_seqlens is NULL", fn);
+        if (n_tok - n_seq_decode < n_chunk)
+            return fail(ATTN_E_SHAPE, "%s: %d rows cannot hold %d decode rows and %d chunks",
+                        fn, n_tok, n_seq_decode, n_chunk);
+        if (max_q_len <= 0 || max_q_len > n_tok - n_seq_decode)
+            return fail(ATTN_E_SHAPE, "%s: max_q_len %d outside 1 .. n_tok - n_seq_decode (%d)",
+                        fn, max_q_len, n_tok - n_seq_decode);
+        const int g = n_head / n_head_kv;
+        if (g > 128 || 128 % g != 0)
+            return fail(ATTN_E_UNSUPPORTED, "%s: %d query heads per kv head (a divisor of 128)",
+                        fn, g);
+    } else if (n_tok != n_seq_decode) {
+        return fail(ATTN_E_SHAPE, "%s: a step of decode rows only has n_tok == n_seq (%d, %d)",
+                    fn, n_tok, n_seq);
+    }
+
+    hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    if (ev0)
+        (void)hipEventRecord(ev0, stream);
+    // Decode half: sequences 0 .. n_seq_decode - 1, one row each, at token
+    // rows 0 .. n_seq_decode - 1 (the step is ordered decode-first).
+    if (n_seq_decode > 0) {
+        rc = split_call(fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                        max_pages_per_seq, ctx_lens, n_seq_decode, n_head, n_head_kv, head_dim,
+                        page_size, kv_dtype, out, workspace, workspace_bytes, stream);
+        if (rc != ATTN_OK)
+            return rc;
+    }
+    // Chunk half: the remaining sequences, their token rows given by the
+    // absolute offsets cu_seqlens[n_seq_decode ..] into the same q and out.
+    if (n_chunk > 0) {
+        pa::PrefillArgs a;
+        a.q = q;
+        a.n_rows = 0;
+        a.k_pool = k_pool;
+        a.v_pool = v_pool;
+        a.k_scale = k_scale;
+        a.v_scale = v_scale;
+        a.n_pages = n_pages;
+        a.block_table = block_table + (int64_t)n_seq_decode * max_pages_per_seq;
+        a.max_pages = max_pages_per_seq;
+        a.ctx_len = 0;
+        a.n_head = n_head;
+        a.n_head_kv = n_head_kv;
+        a.head_dim = head_dim;
+        a.fp8 = kv_dtype == ATTN_KV_FP8_E4M3;
+        a.out = out;
+        a.ev_start = a.ev_stop = nullptr;
+        a.cu_seqlens = cu_seqlens + n_seq_decode;
+        a.ctx_lens = ctx_lens + n_seq_decode;
+        a.n_var = n_chunk;
+        a.max_q_len = max_q_len;
+        a.n_tok = n_tok;
+        rc = from_hip(pa::launch_prefill(a, stream), fn);
+        if (rc != ATTN_OK)
+            return rc;
+    }
+    if (ev1)
+        (void)hipEventRecord(ev1, stream);
+    return ok();
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,

@@ -73,6 +73,17 @@ struct PrefillArgs {
     int fp8;
     void* out;
     hipEvent_t ev_start, ev_stop;
+    // Several sequences in one launch (the chunk half of a mixed step).  When
+    // cu_seqlens is set, sequence i of the launch owns token rows
+    // cu_seqlens[i] .. cu_seqlens[i + 1] - 1 of q and out, has ctx_lens[i]
+    // keys and block-table row i; n_rows and ctx_len are then unused.  A
+    // sequence whose entries are out of range (rows outside 1 .. max_q_len or
+    // past n_tok, ctx_len below its rows or past the table) is skipped.
+    const int32_t* cu_seqlens;  // device, n_var + 1 entries, or null
+    const int32_t* ctx_lens;    // device, n_var entries
+    int32_t n_var;              // sequences of the launch
+    int32_t max_q_len;          // bound on any sequence's rows (sizes the grid)
+    int32_t n_tok;              // token rows of q and out
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

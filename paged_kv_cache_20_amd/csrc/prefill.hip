@@ -257,25 +257,46 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 15, kb = lane >> 4;
     const int Hk = a.n_head_kv, H = a.n_head, g = H / Hk, BP = G::ROWS / g;
-    const int npb = (a.n_rows + BP - 1) / BP;
-    const int nblk = npb * Hk;
-    // XCD-aware placement: consecutive list entries (same kv head) go to the
-    // same XCD; heavier (later) position blocks first within a kv head.
+    // The workgroup's sequence: its rows, keys, first token row and table.
+    int n_rows = a.n_rows, ctx_len = a.ctx_len;
+    int64_t tok0 = 0;
+    const int32_t* bt = a.block_table;
+    // Blocks per sequence: position blocks (of the longest sequence) x kv heads.
+    const int npbm = ((a.cu_seqlens ? a.max_q_len : a.n_rows) + BP - 1) / BP;
+    const int nblk = (a.cu_seqlens ? a.n_var : 1) * npbm * Hk;
+    // XCD-aware placement: consecutive list entries (same sequence and kv
+    // head) go to the same XCD; heavier (later) position blocks first.
     const int per_xcd = (nblk + 7) / 8;
     const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (L >= nblk)
         return;
-    const int kh = L / npb;
-    const int pb = npb - 1 - (L - kh * npb);
+    const int sv = L / (npbm * Hk);
+    const int rem = L - sv * (npbm * Hk);
+    if (a.cu_seqlens) {
+        const int c0 = a.cu_seqlens[sv], c1 = a.cu_seqlens[sv + 1];
+        ctx_len = a.ctx_lens[sv];
+        n_rows = c1 - c0;
+        if (c0 < 0 || c1 > a.n_tok || n_rows < 1 || n_rows > a.max_q_len || ctx_len < n_rows ||
+            (int64_t)ctx_len > (int64_t)a.max_pages * 16)
+            return;
+        tok0 = c0;
+        bt = a.block_table + (int64_t)sv * a.max_pages;
+    }
+    const int npb = (n_rows + BP - 1) / BP;
+    const int kh = rem / npbm;
+    const int pbi = rem - kh * npbm;
+    if (pbi >= npb)
+        return;
+    const int pb = npb - 1 - pbi;
 
     Blk b;
-    b.C = a.ctx_len;
+    b.C = ctx_len;
     b.kh = kh;
     b.Hk = Hk;
     b.n_pages = a.n_pages;
-    b.bt = a.block_table;
-    const int base_pos = a.ctx_len - a.n_rows;
-    const int rlast = min(a.n_rows, (pb + 1) * BP) - 1;
+    b.bt = bt;
+    const int base_pos = ctx_len - n_rows;
+    const int rlast = min(n_rows, (pb + 1) * BP) - 1;
     const int maxpos = base_pos + rlast;  // last key any row here needs
     const int minpos = base_pos + pb * BP;
     const int nt = (maxpos + kKT) / kKT;
@@ -289,10 +310,10 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         const int hg = wrow / BP, p = wrow - hg * BP;
         row[rt] = pb * BP + p;
         head[rt] = kh * g + hg;
-        const bool valid = row[rt] < a.n_rows;
+        const bool valid = row[rt] < n_rows;
         pos[rt] = valid ? base_pos + row[rt] : -1;
         const uint16_t* q =
-            (const uint16_t*)a.q + ((int64_t)(valid ? row[rt] : 0) * H + head[rt]) * D;
+            (const uint16_t*)a.q + ((tok0 + (valid ? row[rt] : 0)) * H + head[rt]) * D;
 #pragma unroll
         for (int st = 0; st < G::KSTEPS; ++st)
             qop[rt][st] = valid ? *(const u32x4*)(q + 32 * st + 8 * kb) : u32x4{0u, 0u, 0u, 0u};
@@ -572,9 +593,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const float inv = 1.f / row_sum4(l[rt]);
-        if (row[rt] >= a.n_rows)
+        if (row[rt] >= n_rows)
             continue;
-        uint16_t* out = (uint16_t*)a.out + ((int64_t)row[rt] * H + head[rt]) * D;
+        uint16_t* out = (uint16_t*)a.out + ((tok0 + row[rt]) * H + head[rt]) * D;
 #pragma unroll
         for (int jb = 0; jb < G::DBLK; ++jb) {
             const int d = 16 * jb + 4 * kb;
@@ -592,9 +613,11 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream)
     using G = PGeo<D, FP8, RT, NW>;
     const int g = a.n_head / a.n_head_kv;
     const int BP = G::ROWS / g;
-    const int npb = (a.n_rows + BP - 1) / BP;
-    const int nblk = npb * a.n_head_kv;
-    const int grid = ((nblk + 7) / 8) * 8;
+    const int npbm = ((a.cu_seqlens ? a.max_q_len : a.n_rows) + BP - 1) / BP;
+    const int64_t nblk = (int64_t)(a.cu_seqlens ? a.n_var : 1) * npbm * a.n_head_kv;
+    if (nblk > (int64_t)1 << 30)
+        return hipErrorInvalidValue;
+    const int grid = (int)((nblk + 7) / 8) * 8;
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, stream);
     hipLaunchKernelGGL((prefill_kernel<D, FP8, RT, NW>), dim3(grid), dim3(G::NTH), 0, stream, a);

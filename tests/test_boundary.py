@@ -125,6 +125,45 @@ def test_prefill_host_checks(pa, over, code, needle):
     assert needle in str(e.value)
 
 
+def mixed_args(**over):
+    a = dict(q=FAKE, n_tok=4104, cu_seqlens=FAKE, n_seq=9, n_seq_decode=8, max_q_len=4096,
+             k_pool=FAKE, v_pool=FAKE, k_scale=None, v_scale=None, n_pages=4096,
+             block_table=FAKE, max_pages_per_seq=2048, ctx_lens=FAKE, n_head=16, n_head_kv=4,
+             head_dim=256, page_size=16, kv_dtype=0, out=FAKE, workspace=FAKE,
+             workspace_bytes=1 << 30, stream=0)
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(n_tok=0), -2, "zero rows"),
+    (dict(n_seq=0), -2, "zero sequences"),
+    (dict(n_seq_decode=10), -2, "n_seq_decode 10"),
+    (dict(n_seq_decode=-1), -2, "n_seq_decode -1"),
+    (dict(cu_seqlens=None), -1, "cu_seqlens is NULL"),
+    (dict(ctx_lens=None), -1, "ctx_lens is NULL"),
+    (dict(max_q_len=0), -2, "max_q_len 0"),
+    (dict(max_q_len=4097), -2, "max_q_len 4097"),
+    (dict(n_tok=8), -2, "cannot hold"),
+    (dict(n_seq=8, n_tok=9), -2, "decode rows only"),
+    (dict(n_head=6, n_head_kv=4), -2, "not a multiple"),
+    (dict(n_head=12, n_head_kv=4), -3, "query heads per kv head"),
+    (dict(head_dim=64), -3, "head_dim 64"),
+    (dict(workspace_bytes=100), -4, "workspace has 100 bytes"),
+    (dict(q=None), -1, "q is NULL"),
+])
+def test_mixed_host_checks(pa, over, code, needle):
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_mixed(**mixed_args(**over))
+    assert e.value.code == code
+    assert needle in str(e.value)
+
+
+def test_mixed_workspace_is_the_decode_halfs(pa):
+    assert pa.attn_paged_workspace_bytes(3, 8, 2048, 16, 256) == \
+        pa.attn_paged_workspace_bytes(0, 8, 2048, 16, 256)
+
+
 @pytest.mark.parametrize("over,code,needle", [
     (dict(n_tok=0), -2, "zero rows"),
     (dict(k_new=None), -1, "k_new"),
