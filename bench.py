@@ -135,6 +135,26 @@ def traffic_from_profiles(kernel_key):
     return e.get("bytes_per_launch")
 
 
+def mixed_inputs(torch, synth, seed=1006):
+    """A continuous-batching step: 256 decode sequences of the fp8 decode
+    workload's shape (H 32 / Hk 8, d 128, fp8 e4m3, lengths log-uniform in
+    [2048, 32768], drawn with `seed` on the CPU) followed by one 2048-row
+    prefill chunk after 6144 cached rows of the same layer."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    dec = synth.scaled(synth.WORKLOADS["decode_256seq_fp8"], seed=seed)
+    lens = synth.draw_lengths(dec, gen).tolist() + [8192]
+    w = synth.listed("mixed_256dec_fp8_plus_2048chunk", lens, 1, 32, 8, 128, True, seed)
+    inp = synth.draw(w, "cuda")
+    q_rows = [1] * 256 + [2048]
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(seed + 1)
+    q = synth.normal_bf16((sum(q_rows), 32, 128), gq)
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(q_rows)), dtype=torch.int32,
+                      device="cuda")
+    return w, inp, q, cu, lens
+
+
 class Bench:
     def __init__(self, torch, pa, synth):
         self.torch, self.pa, self.synth = torch, pa, synth
@@ -222,6 +242,63 @@ class Bench:
         pa.attn_paged_prefill(st["q"], w.rows, st["k"], st["v"], st["ks"], st["vs"],
                               inp.n_pages, inp.table, w.max_pages, st["C"], w.n_head,
                               w.n_head_kv, w.head_dim, 16, st["kv"], st["out"])
+
+    def time_mixed(self, steps=20, warmup=5):
+        """The mixed step as one attn_paged_mixed call, against its decode
+        half (attn_paged_decode) and its chunk half (attn_paged_prefill)
+        called alone."""
+        torch, pa, synth = self.torch, self.pa, self.synth
+        w, inp, q, cu, lens = mixed_inputs(torch, synth)
+        k, v, ks, vs = synth.poison_pools(inp.n_pages, w, "cuda")
+        kv = pa.KV_FP8_E4M3
+        pa.attn_kv_append(inp.k_src, inp.v_src, inp.slots, inp.slots.numel(), k, v, ks, vs,
+                          inp.n_pages, w.n_head_kv, w.head_dim, 16, kv)
+        mp = inp.table.shape[1]
+        wsb = pa.attn_paged_workspace_bytes(3, 256, mp, w.n_head, w.head_dim)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+        n_tok = int(q.shape[0])
+
+        def mixed():
+            pa.attn_paged_mixed(q, n_tok, cu, 257, 256, 2048, k, v, ks, vs, inp.n_pages,
+                                inp.table, mp, inp.lengths, w.n_head, w.n_head_kv, w.head_dim,
+                                16, kv, out, ws, wsb)
+
+        def dec_half():
+            pa.attn_paged_decode(q[:256].view(256, 1, w.n_head, w.head_dim), k, v, ks, vs,
+                                 inp.n_pages, inp.table, mp, inp.lengths, 256, w.n_head,
+                                 w.n_head_kv, w.head_dim, 16, kv, out[:256], ws, wsb)
+
+        def chunk_half():
+            pa.attn_paged_prefill(q[256:], 2048, k, v, ks, vs, inp.n_pages, inp.table[256], mp,
+                                  8192, w.n_head, w.n_head_kv, w.head_dim, 16, kv, out[256:])
+
+        res = {}
+        for tag, fn in (("mixed_call", mixed), ("decode_half", dec_half),
+                        ("chunk_half", chunk_half)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            # The library launches on torch's current stream, so torch's
+            # events bracket each whole call (all of its kernels).
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            for i in range(steps):
+                evs[i][0].record()
+                fn()
+                evs[i][1].record()
+            torch.cuda.synchronize()
+            kern = sorted(a.elapsed_time(b) for a, b in evs)
+            res[tag] = kern[len(kern) // 2] * 1e3
+        dw = synth.scaled(synth.WORKLOADS["decode_256seq_fp8"], n_seq=256)
+        by = decode_bytes(lens[:256], dw, with_out=False)
+        fl = prefill_flops(2048, 8192, w)
+        return {"us_median": round(res["mixed_call"], 2),
+                "decode_half_alone_us": round(res["decode_half"], 2),
+                "chunk_half_alone_us": round(res["chunk_half"], 2),
+                "decode_bytes": by, "chunk_flops": fl,
+                "note": "medians of whole-call spans (every kernel of the call) by events on "
+                        "the call's stream"}
 
     def time_prefill(self, st, steps, warmup):
         torch = self.torch
@@ -404,6 +481,13 @@ def main():
                 sec[other] = {"error": str(e)[:200]}
             torch.cuda.empty_cache()
             log("[bench] secondary done", other, sec[other])
+        log("[bench] secondary mixed_256dec_fp8_plus_2048chunk")
+        try:
+            sec["mixed_256dec_fp8_plus_2048chunk"] = b.time_mixed()
+        except Exception as e:  # report, keep the headline
+            sec["mixed_256dec_fp8_plus_2048chunk"] = {"error": str(e)[:200]}
+        torch.cuda.empty_cache()
+        log("[bench] secondary done", sec["mixed_256dec_fp8_plus_2048chunk"])
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
 
