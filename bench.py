@@ -300,6 +300,42 @@ class Bench:
                 "note": "medians of whole-call spans (every kernel of the call) by events on "
                         "the call's stream"}
 
+    def time_widths(self, widths=(1, 2, 4, 8), steps=20, warmup=5):
+        """Rounds of several widths over the 32-sequence verify cache (d 256,
+        bf16, 4,104 tokens each): split-kernel time per width (HIP events
+        from the library's kernel timer) and the bytes it streams."""
+        torch, pa = self.torch, self.pa
+        st = self.setup_split("verify_32seq_8rows")
+        w, inp = st["w"], st["inp"]
+        res = {}
+        for width in widths:
+            q = inp.q[:, :width].contiguous()
+            out = torch.empty_like(q)
+
+            def call():
+                pa.attn_paged_verify_width(q, st["k"], st["v"], st["ks"], st["vs"], inp.n_pages,
+                                           inp.table, w.max_pages, inp.lengths, w.n_seq, width,
+                                           w.n_head, w.n_head_kv, w.head_dim, 16, st["kv"], out,
+                                           st["ws"], st["wsb"])
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
+            for i in range(steps):
+                pa.attn_set_kernel_timer(evs[i][0], evs[i][1])
+                call()
+            torch.cuda.synchronize()
+            kern = sorted(self.ev.elapsed_ms(a, b) for a, b in evs)
+            for a, b in evs:
+                self.ev.destroy(a)
+                self.ev.destroy(b)
+            by = decode_bytes(st["lengths_host"], self.synth.scaled(w, rows=width),
+                              with_out=False)
+            us = kern[len(kern) // 2] * 1e3
+            res["w%d" % width] = {"kernel_median_us": round(us, 2), "bytes": by,
+                                  "hbm_frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        return res
+
     def time_prefill(self, st, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
@@ -481,6 +517,13 @@ def main():
                 sec[other] = {"error": str(e)[:200]}
             torch.cuda.empty_cache()
             log("[bench] secondary done", other, sec[other])
+        log("[bench] secondary verify widths")
+        try:
+            sec["verify_32seq_widths_1_2_4_8"] = b.time_widths()
+        except Exception as e:  # report, keep the headline
+            sec["verify_32seq_widths_1_2_4_8"] = {"error": str(e)[:200]}
+        torch.cuda.empty_cache()
+        log("[bench] secondary done", sec["verify_32seq_widths_1_2_4_8"])
         log("[bench] secondary mixed_256dec_fp8_plus_2048chunk")
         try:
             sec["mixed_256dec_fp8_plus_2048chunk"] = b.time_mixed()

@@ -156,6 +156,30 @@ int attn_paged_verify(const void* q, const void* k_pool, const void* v_pool,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_paged_verify_width -- a speculative round of `width` rows per sequence,
+ * 1 <= width <= ATTN_VERIFY_ROWS, causal within the round and after the
+ * cached context ("TandemLLM -- Adding a model", section "The adapter path
+ * in ten steps": a recorded decode is replayed as chains of every verify
+ * width and every row must match bit for bit).
+ *
+ *   q, out     bf16 [n_seq][width][n_head][head_dim]
+ *   workspace  attn_paged_workspace_bytes(1, ...) covers every width
+ * Row r of sequence s is at position ctx_lens[s] - width + r; its result
+ * equals, bit for bit, attn_paged_decode of that row with ctx_len =
+ * position + 1 over the same cache (width 8 is attn_paged_verify, width 1
+ * is attn_paged_decode).  Needs ctx_lens[s] >= width and, besides the
+ * decode limits, ceil(width / floor(16 / g)) * head_dim <= 512 after
+ * rounding the tile count up to 1, 2 or 4.
+ */
+int attn_paged_verify_width(const void* q, const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale, int64_t n_pages,
+                            const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* ctx_lens, int32_t n_seq, int32_t width,
+                            int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+                            int32_t page_size, attn_kv_dtype kv_dtype, void* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_paged_prefill -- a chunk of n_rows new rows of ONE sequence over its
  * cached context ("kern manifest v7" schema, $defs.Batch: rows given by the
  * chunk, one sequence; `context` is the cached rows it expands over).

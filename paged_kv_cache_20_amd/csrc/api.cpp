@@ -259,6 +259,24 @@ int attn_paged_verify(const void* q, const void* k_pool, const void* v_pool,
                       stream);
 }
 
+int attn_paged_verify_width(const void* q, const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale, int64_t n_pages,
+                            const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* ctx_lens, int32_t n_seq, int32_t width,
+                            int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+                            int32_t page_size, attn_kv_dtype kv_dtype, void* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char* fn = "attn_paged_verify_width";
+    if (width <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (width = %d)", fn, width);
+    if (width > ATTN_VERIFY_ROWS)
+        return fail(ATTN_E_UNSUPPORTED, "%s: width %d above %d", fn, width, ATTN_VERIFY_ROWS);
+    return split_call(fn, width, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                      max_pages_per_seq, ctx_lens, n_seq, n_head, n_head_kv, head_dim, page_size,
+                      kv_dtype, out, workspace, workspace_bytes, stream);
+}
+
 int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const void* v_pool,
                        const float* k_scale, const float* v_scale, int64_t n_pages,
                        const int32_t* block_table, int32_t max_pages_per_seq, int32_t ctx_len,

@@ -95,6 +95,25 @@ def test_decode_host_checks(pa, over, code, needle):
     assert needle in str(e.value)
 
 
+@pytest.mark.parametrize("width,code,needle", [
+    (0, -2, "zero rows"), (-3, -2, "zero rows"), (9, -3, "width 9"),
+])
+def test_verify_width_host_checks(pa, width, code, needle):
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_verify_width(**decode_args(width=width))
+    assert e.value.code == code
+    assert needle in str(e.value)
+
+
+def test_verify_width_rejects_unserved_group(pa):
+    # width 5 with 4 heads per kv head at head_dim 256: 2 tiles x 256 fits,
+    # 16 heads per kv head: 5 tiles -> 8 x 256 does not
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_verify_width(**decode_args(width=5, n_head=32, n_head_kv=2,
+                                                 head_dim=256))
+    assert e.value.code == pa.ATTN_E_UNSUPPORTED
+
+
 def test_verify_rejects_unserved_group(pa):
     # 16 heads per kv head at head_dim 256: 8 tiles x 256 > 512 accumulator columns
     with pytest.raises(pa.AttnError) as e:
