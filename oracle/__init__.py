@@ -57,6 +57,9 @@ def _load():
         lib.oracle_paged_attention.argtypes = [
             P, i32, i32, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, P, P, i32]
         lib.oracle_paged_attention.restype = ctypes.c_int
+        lib.oracle_paged_attention_window.argtypes = [
+            P, i32, i32, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32, P, P, P, i32]
+        lib.oracle_paged_attention_window.restype = ctypes.c_int
         lib.oracle_kv_append.argtypes = [P, P, P, i32, P, P, P, P, i64, i32, i32, i32, i32]
         lib.oracle_kv_append.restype = ctypes.c_int
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
@@ -84,13 +87,14 @@ def default_threads() -> int:
 
 def paged_attention(q, k_pool, v_pool, block_table, ctx_lens, *, n_head, n_head_kv, head_dim,
                     page_size, kv_dtype=KV_BF16, k_scale=None, v_scale=None, row_mask=None,
-                    threads=None) -> np.ndarray:
+                    window=0, kv_floor=None, threads=None) -> np.ndarray:
     """fp64 attention of every row of ``q`` (uint16 bf16 bits, shape
     [n_seq, rows, n_head, head_dim]) over the paged pools.
 
-    Row r of sequence s attends to key positions 0 .. ctx_lens[s]-rows+r.
-    ``row_mask`` ([n_seq, rows], nonzero = compute) limits the work; skipped
-    rows come back as NaN.
+    Row r of sequence s sits at position p = ctx_lens[s]-rows+r and attends
+    to key positions max(kv_floor[s], p-window+1) .. p (window 0: no window;
+    kv_floor None: floor 0).  ``row_mask`` ([n_seq, rows], nonzero =
+    compute) limits the work; skipped rows come back as NaN.
     """
     lib = _load()
     q = _c(q, np.uint16)
@@ -110,11 +114,13 @@ def paged_attention(q, k_pool, v_pool, block_table, ctx_lens, *, n_head, n_head_
         assert ks is not None and vs is not None and ks.shape == (n_pages, n_head_kv)
     mask = None if row_mask is None else _c(np.asarray(row_mask).reshape(n_seq * rows) != 0,
                                             np.uint8)
+    fl = None if kv_floor is None else _c(kv_floor, np.int32)
+    assert fl is None or fl.shape == (n_seq,)
     out = np.full(q.shape, np.nan, dtype=np.float64)
-    rc = lib.oracle_paged_attention(
+    rc = lib.oracle_paged_attention_window(
         _ptr(q), n_seq, rows, _ptr(kp), _ptr(vp), _ptr(ks), _ptr(vs), n_pages, _ptr(bt),
-        bt.shape[1], _ptr(cl), n_head, n_head_kv, head_dim, page_size, kv_dtype, _ptr(mask),
-        _ptr(out), threads or default_threads())
+        bt.shape[1], _ptr(cl), n_head, n_head_kv, head_dim, page_size, kv_dtype, int(window),
+        _ptr(fl), _ptr(mask), _ptr(out), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_paged_attention failed with %d" % rc)
     return out

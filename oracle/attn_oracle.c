@@ -109,18 +109,19 @@ static double orc_elem(const orc_pool *pl, int is_v, int64_t page, int kh, int o
 }
 
 /*
- * Attention of one query vector over key positions 0..last of sequence seq,
- * kv head kh.  Writes d doubles to out.  Returns 0, or -1 when a block-table
- * entry that the row needs is outside the pool.
+ * Attention of one query vector over key positions first..last of sequence
+ * seq, kv head kh.  Writes d doubles to out.  Returns 0, or -1 when a
+ * block-table entry that the row needs is outside the pool.  (scores is
+ * indexed by absolute position; entries below first are not used.)
  */
-static int orc_attend(const orc_pool *pl, const double *q, int seq, int64_t last, int kh,
-                      double *scores, double *out)
+static int orc_attend(const orc_pool *pl, const double *q, int seq, int64_t first, int64_t last,
+                      int kh, double *scores, double *out)
 {
     const int d = pl->d, P = pl->P;
     const double inv_sqrt_d = 1.0 / sqrt((double)d);
     int64_t t;
     int i;
-    for (t = 0; t <= last; ++t) {
+    for (t = first; t <= last; ++t) {
         int64_t page = pl->block_table[(int64_t)seq * pl->max_pages + t / P];
         double dot = 0.0;
         if (page < 0 || page >= pl->n_pages)
@@ -130,17 +131,17 @@ static int orc_attend(const orc_pool *pl, const double *q, int seq, int64_t last
         scores[t] = dot * inv_sqrt_d;
     }
     double mx = -INFINITY;
-    for (t = 0; t <= last; ++t)
+    for (t = first; t <= last; ++t)
         if (scores[t] > mx)
             mx = scores[t];
     double z = 0.0;
-    for (t = 0; t <= last; ++t) {
+    for (t = first; t <= last; ++t) {
         scores[t] = exp(scores[t] - mx);
         z += scores[t];
     }
     for (i = 0; i < d; ++i)
         out[i] = 0.0;
-    for (t = 0; t <= last; ++t) {
+    for (t = first; t <= last; ++t) {
         int64_t page = pl->block_table[(int64_t)seq * pl->max_pages + t / P];
         double w = scores[t] / z;
         for (i = 0; i < d; ++i)
@@ -164,13 +165,24 @@ static int orc_attend(const orc_pool *pl, const double *q, int seq, int64_t last
  * the call's rows or longer than its block-table row, -3 for a block-table
  * entry outside the pool.
  */
-int oracle_paged_attention(const uint16_t *q, int n_seq, int rows,
-                           const void *k_pool, const void *v_pool,
-                           const float *k_scale, const float *v_scale, int64_t n_pages,
-                           const int32_t *block_table, int max_pages,
-                           const int32_t *ctx_lens, int n_head, int n_head_kv,
-                           int head_dim, int page_size, int kv_dtype,
-                           const uint8_t *row_mask, double *out, int n_threads)
+/*
+ * oracle_paged_attention_window -- the same with a lower bound on the keys
+ * a row attends ("Radiance Architecture Plugins -- declaring a model",
+ * section "Declare: buffers and KV groups": a KV group bounded by a window,
+ * and a ring whose window floor is set at runtime).  The row at position p
+ * attends keys max(kv_floor[s], p - window + 1) .. p; window 0 means no
+ * window, kv_floor NULL a floor of 0.  Returns -2 also for a floor outside
+ * 0 .. ctx_lens[s] - rows.  Block-table entries below a row's first key are
+ * not read.
+ */
+int oracle_paged_attention_window(const uint16_t *q, int n_seq, int rows,
+                                  const void *k_pool, const void *v_pool,
+                                  const float *k_scale, const float *v_scale, int64_t n_pages,
+                                  const int32_t *block_table, int max_pages,
+                                  const int32_t *ctx_lens, int n_head, int n_head_kv,
+                                  int head_dim, int page_size, int kv_dtype, int window,
+                                  const int32_t *kv_floor, const uint8_t *row_mask, double *out,
+                                  int n_threads)
 {
     if (n_seq <= 0 || rows <= 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 ||
         page_size <= 0 || n_head % n_head_kv != 0)
@@ -180,8 +192,12 @@ int oracle_paged_attention(const uint16_t *q, int n_seq, int rows,
                    max_pages, n_head_kv, head_dim, page_size, kv_dtype};
     const int g = n_head / n_head_kv;
     int64_t max_ctx = 0;
+    if (window < 0)
+        return -1;
     for (int s = 0; s < n_seq; ++s) {
         if (ctx_lens[s] < rows || (int64_t)ctx_lens[s] > (int64_t)max_pages * page_size)
+            return -2;
+        if (kv_floor && (kv_floor[s] < 0 || kv_floor[s] > ctx_lens[s] - rows))
             return -2;
         if (ctx_lens[s] > max_ctx)
             max_ctx = ctx_lens[s];
@@ -205,7 +221,10 @@ int oracle_paged_attention(const uint16_t *q, int n_seq, int rows,
             for (int i = 0; i < head_dim; ++i)
                 qrow[i] = orc_bf16(qv[i]);
             const int64_t last = (int64_t)ctx_lens[s] - rows + r;
-            if (orc_attend(&pl, qrow, s, last, h / g, scores, out + it * head_dim) != 0) {
+            int64_t first = kv_floor ? kv_floor[s] : 0;
+            if (window > 0 && last - window + 1 > first)
+                first = last - window + 1;
+            if (orc_attend(&pl, qrow, s, first, last, h / g, scores, out + it * head_dim) != 0) {
 #pragma omp atomic write
                 status = -3;
             }
@@ -214,6 +233,20 @@ int oracle_paged_attention(const uint16_t *q, int n_seq, int rows,
         free(qrow);
     }
     return status;
+}
+
+int oracle_paged_attention(const uint16_t *q, int n_seq, int rows,
+                           const void *k_pool, const void *v_pool,
+                           const float *k_scale, const float *v_scale, int64_t n_pages,
+                           const int32_t *block_table, int max_pages,
+                           const int32_t *ctx_lens, int n_head, int n_head_kv,
+                           int head_dim, int page_size, int kv_dtype,
+                           const uint8_t *row_mask, double *out, int n_threads)
+{
+    return oracle_paged_attention_window(q, n_seq, rows, k_pool, v_pool, k_scale, v_scale,
+                                         n_pages, block_table, max_pages, ctx_lens, n_head,
+                                         n_head_kv, head_dim, page_size, kv_dtype, 0, NULL,
+                                         row_mask, out, n_threads);
 }
 
 /* ---------------------------------------------------------------------- */
