@@ -238,6 +238,49 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Windowed and ring KV groups ("Radiance Architecture Plugins -- declaring a
+ * model", section "Declare: buffers and KV groups": a KV group bounded by a
+ * window, and a ring whose window floor is set at runtime).  A row at
+ * position p attends keys lo .. p with
+ *     lo = max(kv_floor, p - window + 1)      (window 0: no window)
+ * Pages wholly below the first key a call's rows attend are neither read
+ * nor checked, so a ring may have released them (their block-table entries
+ * may hold anything).  A row's result depends only on its own position,
+ * window and floor: every row of attn_paged_decode_window with `rows` rows
+ * equals, bit for bit, the 1-row call at its position with the same window
+ * and floor, and window 0 with floor 0 is the plain call.
+ *
+ * attn_paged_decode_window -- decode (rows = 1) or a round of rows <= 8,
+ * layout and limits as attn_paged_verify_width.
+ *   kv_floor  int32 [n_seq], DEVICE, or NULL (floor 0).  A floor outside
+ *             0 .. ctx_lens[s] - rows gives NaN in every element of the
+ *             sequence's rows.
+ *   window    HOST value >= 0.
+ */
+int attn_paged_decode_window(const void* q, int32_t rows, const void* k_pool,
+                             const void* v_pool, const float* k_scale, const float* v_scale,
+                             int64_t n_pages, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t n_seq,
+                             int32_t window, const int32_t* kv_floor, int32_t n_head,
+                             int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                             attn_kv_dtype kv_dtype, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_paged_prefill_window -- attn_paged_prefill with the window and floor
+ * above; window and kv_floor are HOST values, checked: window >= 0 and
+ * 0 <= kv_floor <= ctx_len - n_rows.
+ */
+int attn_paged_prefill_window(const void* q, int32_t n_rows, const void* k_pool,
+                              const void* v_pool, const float* k_scale, const float* v_scale,
+                              int64_t n_pages, const int32_t* block_table,
+                              int32_t max_pages_per_seq, int32_t ctx_len, int32_t window,
+                              int32_t kv_floor, int32_t n_head, int32_t n_head_kv,
+                              int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * attn_kv_append -- write n_tok new K/V rows into their token slots
  * ("kern manifest v7" schema, $defs.Fill "slot": each row's token slot in
  * the paged state; slot = page * page_size + offset).  A negative slot skips

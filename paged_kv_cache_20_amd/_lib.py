@@ -33,7 +33,8 @@ ATTN_E_DEVICE = -6
 
 EXPORTS = [
     "attn_paged_decode", "attn_paged_verify", "attn_paged_verify_width", "attn_paged_prefill",
-    "attn_paged_mixed", "attn_kv_append", "attn_block_table_build", "attn_paged_workspace_bytes", "attn_caps",
+    "attn_paged_mixed", "attn_paged_decode_window", "attn_paged_prefill_window",
+    "attn_kv_append", "attn_block_table_build", "attn_paged_workspace_bytes", "attn_caps",
     "attn_check_lengths_host", "attn_check_block_table_host", "attn_last_error",
     "attn_set_kernel_timer", "attn_set_max_workgroups",
 ]
@@ -71,6 +72,13 @@ _lib.attn_paged_prefill.restype = ctypes.c_int
 _lib.attn_paged_mixed.argtypes = [_P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _P, _I64, _P, _I32,
                                   _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]
 _lib.attn_paged_mixed.restype = ctypes.c_int
+_lib.attn_paged_decode_window.argtypes = [_P, _I32, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                          _I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
+                                          _P]
+_lib.attn_paged_decode_window.restype = ctypes.c_int
+_lib.attn_paged_prefill_window.argtypes = [_P, _I32, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                           _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]
+_lib.attn_paged_prefill_window.restype = ctypes.c_int
 _lib.attn_kv_append.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                 _P]
 _lib.attn_kv_append.restype = ctypes.c_int
@@ -166,6 +174,28 @@ def attn_paged_verify_width(q, k_pool, v_pool, k_scale, v_scale, n_pages, block_
         _dp(q), _dp(k_pool), _dp(v_pool), _dp(k_scale), _dp(v_scale), n_pages, _dp(block_table),
         max_pages_per_seq, _dp(ctx_lens), n_seq, width, n_head, n_head_kv, head_dim, page_size,
         kv_dtype, _dp(out), _dp(workspace), workspace_bytes, _stream(stream)))
+
+
+def attn_paged_decode_window(q, rows, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                             max_pages_per_seq, ctx_lens, n_seq, window, kv_floor, n_head,
+                             n_head_kv, head_dim, page_size, kv_dtype, out, workspace=None,
+                             workspace_bytes=0, stream=None):
+    return _check(_lib.attn_paged_decode_window(
+        _dp(q), rows, _dp(k_pool), _dp(v_pool), _dp(k_scale), _dp(v_scale), n_pages,
+        _dp(block_table), max_pages_per_seq, _dp(ctx_lens), n_seq, window, _dp(kv_floor), n_head,
+        n_head_kv, head_dim, page_size, kv_dtype, _dp(out), _dp(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def attn_paged_prefill_window(q, n_rows, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                              max_pages_per_seq, ctx_len, window, kv_floor, n_head, n_head_kv,
+                              head_dim, page_size, kv_dtype, out, workspace=None,
+                              workspace_bytes=0, stream=None):
+    return _check(_lib.attn_paged_prefill_window(
+        _dp(q), n_rows, _dp(k_pool), _dp(v_pool), _dp(k_scale), _dp(v_scale), n_pages,
+        _dp(block_table), max_pages_per_seq, ctx_len, window, kv_floor, n_head, n_head_kv,
+        head_dim, page_size, kv_dtype, _dp(out), _dp(workspace), workspace_bytes,
+        _stream(stream)))
 
 
 def attn_paged_mixed(q, n_tok, cu_seqlens, n_seq, n_seq_decode, max_q_len, k_pool, v_pool,

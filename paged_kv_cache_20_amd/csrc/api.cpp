@@ -132,7 +132,8 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
                const int32_t* block_table, int32_t max_pages, const int32_t* ctx_lens,
                int32_t n_seq, int32_t n_head, int32_t n_head_kv, int32_t head_dim,
                int32_t page_size, attn_kv_dtype kv_dtype, void* out, void* workspace,
-               size_t workspace_bytes, hipStream_t stream)
+               size_t workspace_bytes, hipStream_t stream, int32_t window = 0,
+               const int32_t* kv_floor = nullptr)
 {
     int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                           max_pages, n_head, n_head_kv, head_dim, page_size, kv_dtype, out);
@@ -187,6 +188,8 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     a.ev_stop = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
     a.max_blocks = g_max_workgroups.load(std::memory_order_relaxed);
+    a.window = window;
+    a.kv_floor = kv_floor;
     return from_hip(pa::launch_split_decode(a, stream), fn);
 }
 
@@ -277,14 +280,13 @@ int attn_paged_verify_width(const void* q, const void* k_pool, const void* v_poo
                       kv_dtype, out, workspace, workspace_bytes, stream);
 }
 
-int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const void* v_pool,
-                       const float* k_scale, const float* v_scale, int64_t n_pages,
-                       const int32_t* block_table, int32_t max_pages_per_seq, int32_t ctx_len,
-                       int32_t n_head, int32_t n_head_kv, int32_t head_dim, int32_t page_size,
-                       attn_kv_dtype kv_dtype, void* out, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream)
+static int prefill_call(const char* fn, const void* q, int32_t n_rows, const void* k_pool,
+                        const void* v_pool, const float* k_scale, const float* v_scale,
+                        int64_t n_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                        int32_t ctx_len, int32_t window, int32_t kv_floor, int32_t n_head,
+                        int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                        attn_kv_dtype kv_dtype, void* out, hipStream_t stream)
 {
-    const char* fn = "attn_paged_prefill";
     int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                           max_pages_per_seq, n_head, n_head_kv, head_dim, page_size, kv_dtype,
                           out);
@@ -297,8 +299,11 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
     if ((int64_t)ctx_len > (int64_t)max_pages_per_seq * page_size)
         return fail(ATTN_E_RANGE, "%s: ctx_len %d exceeds max_pages_per_seq * page_size", fn,
                     ctx_len);
-    (void)workspace;
-    (void)workspace_bytes;
+    if (window < 0)
+        return fail(ATTN_E_RANGE, "%s: window %d is negative", fn, window);
+    if (kv_floor < 0 || kv_floor > ctx_len - n_rows)
+        return fail(ATTN_E_RANGE, "%s: kv_floor %d outside 0 .. ctx_len - n_rows (%d)", fn,
+                    kv_floor, ctx_len - n_rows);
     pa::PrefillArgs a;
     a.q = q;
     a.n_rows = n_rows;
@@ -323,7 +328,60 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
     a.n_var = 1;
     a.max_q_len = n_rows;
     a.n_tok = n_rows;
+    a.window = window;
+    a.kv_floor = kv_floor;
     return from_hip(pa::launch_prefill(a, stream), fn);
+}
+
+int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const void* v_pool,
+                       const float* k_scale, const float* v_scale, int64_t n_pages,
+                       const int32_t* block_table, int32_t max_pages_per_seq, int32_t ctx_len,
+                       int32_t n_head, int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                       attn_kv_dtype kv_dtype, void* out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return prefill_call("attn_paged_prefill", q, n_rows, k_pool, v_pool, k_scale, v_scale,
+                        n_pages, block_table, max_pages_per_seq, ctx_len, 0, 0, n_head,
+                        n_head_kv, head_dim, page_size, kv_dtype, out, stream);
+}
+
+int attn_paged_prefill_window(const void* q, int32_t n_rows, const void* k_pool,
+                              const void* v_pool, const float* k_scale, const float* v_scale,
+                              int64_t n_pages, const int32_t* block_table,
+                              int32_t max_pages_per_seq, int32_t ctx_len, int32_t window,
+                              int32_t kv_floor, int32_t n_head, int32_t n_head_kv,
+                              int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return prefill_call("attn_paged_prefill_window", q, n_rows, k_pool, v_pool, k_scale, v_scale,
+                        n_pages, block_table, max_pages_per_seq, ctx_len, window, kv_floor,
+                        n_head, n_head_kv, head_dim, page_size, kv_dtype, out, stream);
+}
+
+int attn_paged_decode_window(const void* q, int32_t rows, const void* k_pool,
+                             const void* v_pool, const float* k_scale, const float* v_scale,
+                             int64_t n_pages, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t n_seq,
+                             int32_t window, const int32_t* kv_floor, int32_t n_head,
+                             int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                             attn_kv_dtype kv_dtype, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream)
+{
+    const char* fn = "attn_paged_decode_window";
+    if (rows <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (rows = %d)", fn, rows);
+    if (rows > ATTN_VERIFY_ROWS)
+        return fail(ATTN_E_UNSUPPORTED, "%s: rows %d above %d", fn, rows, ATTN_VERIFY_ROWS);
+    if (window < 0)
+        return fail(ATTN_E_RANGE, "%s: window %d is negative", fn, window);
+    return split_call(fn, rows, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                      max_pages_per_seq, ctx_lens, n_seq, n_head, n_head_kv, head_dim, page_size,
+                      kv_dtype, out, workspace, workspace_bytes, stream, window, kv_floor);
 }
 
 int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, int32_t n_seq,
@@ -406,6 +464,8 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
         a.n_var = n_chunk;
         a.max_q_len = max_q_len;
         a.n_tok = n_tok;
+        a.window = 0;
+        a.kv_floor = 0;
         rc = from_hip(pa::launch_prefill(a, stream), fn);
         if (rc != ATTN_OK)
             return rc;

@@ -248,9 +248,10 @@ __device__ __forceinline__ int slot_row(int slot, int tau, int g, int ppt, int R
     return r < R ? r : -1;
 }
 
-template <int D, bool FP8, int NT>
+template <int D, bool FP8, int NT, bool WIN>
 __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (&qop)[NT][D / 32],
-                                             const int (&last)[NT], float (&m)[NT], float (&l)[NT],
+                                             const int (&first)[NT], const int (&last)[NT],
+                                             float (&m)[NT], float (&l)[NT],
                                              f32x4 (&O)[NT][D / 16], int kt, float sc0, float sc1,
                                              float vs0, float vs1, int kb)
 {
@@ -286,7 +287,9 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
             for (int r = 0; r < 4; ++r) {
                 const int key = kt + 16 * kblk + 4 * kb + r;
                 const float x = acc[kblk][tau][r] * (kblk ? sc1 : sc0);
-                sv[kblk][r] = key <= last[tau] ? x : neg_inf();
+                // (without a window or floor every first[] is 0: one compare)
+                const bool in = WIN ? key <= last[tau] && key >= first[tau] : key <= last[tau];
+                sv[kblk][r] = in ? x : neg_inf();
                 tmax = fmaxf(tmax, sv[kblk][r]);
             }
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
@@ -387,14 +390,23 @@ __device__ __forceinline__ bool ctx_ok(int C, int R, int64_t cap) { return C >= 
 // A work item resolved to its sequence, split and kv head.
 struct Item {
     int s, j, kh, C, t0, t1, npg;
+    int lo;  // first key the item's rows may attend (window / floor), <= t0 + KT - 1
 };
+
+// First key position row `pos` attends: its sliding window (window > 0)
+// and the sequence's runtime floor, whichever is later.
+__device__ __forceinline__ int key_floor(int pos, int window, int floor_s)
+{
+    return max(floor_s, window > 0 ? pos - window + 1 : 0);
+}
 
 // Items are numbered full splits first (sequence, split, kv head), then the
 // partial last splits (sequence, kv head): a wave's later items are the
 // short ones, so the grid's last round is short.  s_pre / s_pp: exclusive
 // prefixes over sequences of their full / partial items.
+template <int KT>
 __device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, const int* s_len,
-                                             int S, int Hk, int item)
+                                             const int* s_lo, int S, int Hk, int item)
 {
     const int nfull = s_pre[S];
     const bool full = item < nfull;
@@ -412,10 +424,16 @@ __device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, 
     it.s = __builtin_amdgcn_readfirstlane(lo);
     const int local = __builtin_amdgcn_readfirstlane(key - pre[it.s]);
     it.C = __builtin_amdgcn_readfirstlane(s_len[it.s]);
-    it.j = full ? local / Hk : it.C / kChunk;
-    it.kh = full ? local - it.j * Hk : local;
-    it.t0 = it.j * kChunk;
-    it.t1 = min(it.t0 + kChunk, it.C);
+    const int lo_s = __builtin_amdgcn_readfirstlane(s_lo[it.s]);
+    const int j0 = lo_s / kChunk;  // the sequence's first split with keys to attend
+    it.j = full ? j0 + local / Hk : it.C / kChunk;
+    it.kh = full ? local - (local / Hk) * Hk : local;
+    // Tiles keep their absolute grid (a multiple of KT from the split start)
+    // whatever the window, so a row's arithmetic does not depend on it.
+    const int base = it.j * kChunk;
+    it.lo = max(lo_s, base);
+    it.t0 = base + ((it.lo - base) / KT) * KT;
+    it.t1 = min(base + kChunk, it.C);
     it.npg = (it.t1 - it.t0 + 15) >> 4;
     return it;
 }
@@ -430,7 +448,7 @@ __device__ __forceinline__ int fetch_pages(const SplitArgs& a, const Item& it, b
     return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4u, 0, 0);
 }
 
-template <int D, bool FP8, int NT>
+template <int D, bool FP8, int NT, bool WIN>
 __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(SplitArgs a)
 {
     using G = Geo<D, FP8>;
@@ -440,6 +458,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     __shared__ int s_pre[kMaxSeq + 1];  // full items before each sequence
     __shared__ int s_pp[kMaxSeq + 1];   // partial items before each sequence
     __shared__ int s_len[kMaxSeq];
+    __shared__ int s_lo[kMaxSeq];  // first key the sequence's first row attends
     __shared__ int s_tmp[256], s_tmp2[256];
 
     const int S = a.n_seq, R = a.rows, Hk = a.n_head_kv, H = a.n_head;
@@ -450,8 +469,20 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     // Exclusive prefixes over sequences of their full and partial work items,
     // and the lengths (kept in LDS: item set-up then waits on no global load).
     {
-        auto nfull = [&](int C) { return ctx_ok(C, R, cap) ? (C / kChunk) * Hk : 0; };
-        auto npart = [&](int C) { return ctx_ok(C, R, cap) && C % kChunk != 0 ? Hk : 0; };
+        // lo: first key of the sequence's first row; -1 marks a sequence
+        // whose floor lies outside 0 .. that row's position (no items, NaN).
+        auto first_key = [&](int s, int C) {
+            const int f = a.kv_floor ? a.kv_floor[s] : 0;
+            if (f < 0 || f > C - R)
+                return -1;
+            return key_floor(C - R, a.window, f);
+        };
+        auto nfull = [&](int C, int lo) {
+            return ctx_ok(C, R, cap) && lo >= 0 ? (C / kChunk - lo / kChunk) * Hk : 0;
+        };
+        auto npart = [&](int C, int lo) {
+            return ctx_ok(C, R, cap) && lo >= 0 && C % kChunk != 0 ? Hk : 0;
+        };
         const int per = (S + 255) / 256;
         const int b0 = tid * per;
         int loc = 0, loc2 = 0;
@@ -459,8 +490,9 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             const int s = b0 + i;
             if (s < S) {
                 const int C = a.ctx_lens[s];
-                loc += nfull(C);
-                loc2 += npart(C);
+                const int lo = ctx_ok(C, R, cap) ? first_key(s, C) : -1;
+                loc += nfull(C, lo);
+                loc2 += npart(C, lo);
             }
         }
         s_tmp[tid] = loc;
@@ -482,9 +514,11 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
                 s_pre[s] = run;
                 s_pp[s] = run2;
                 const int C = a.ctx_lens[s];
+                const int lo = ctx_ok(C, R, cap) ? first_key(s, C) : -1;
                 s_len[s] = C;
-                run += nfull(C);
-                run2 += npart(C);
+                s_lo[s] = max(lo, 0);
+                run += nfull(C, lo);
+                run2 += npart(C, lo);
             }
         }
         if (tid == 255) {
@@ -514,7 +548,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     // give chunk 0 with no rows, so no load can leave the pool.
     auto page = [&](const Item& I, int pidv, bool live, int e, int64_t& chunk, int& rows) {
         const int p = rdlane(pidv, e);
-        const bool ok = live && e < I.npg && p >= 0 && (int64_t)p < a.n_pages;
+        // Pages wholly below the item's first key are neither read nor
+        // checked (a runtime floor may have released them).
+        const bool below = I.t0 + 16 * e + 16 <= I.lo;
+        const bool ok = live && e < I.npg && !below && p >= 0 && (int64_t)p < a.n_pages;
         chunk = (int64_t)(ok ? p : 0) * Hk + I.kh;
         // (readfirstlane keeps the clamp, which only the vector unit has,
         // from turning the buffer resources into per-lane values.)
@@ -568,10 +605,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     // are not computed), so every item starts at ring slot 0.
     // Table entries are fetched two items ahead and held in registers one
     // item ahead, so the ring never waits for them.
-    Item cur = resolve_item(s_pre, s_pp, s_len, S, Hk, item);
+    Item cur = resolve_item<KT>(s_pre, s_pp, s_len, s_lo, S, Hk, item);
     int pid = fetch_pages(a, cur, true);
     bool has_next = item + nwaves < total;
-    Item nxt = resolve_item(s_pre, s_pp, s_len, S, Hk, has_next ? item + nwaves : item);
+    Item nxt = resolve_item<KT>(s_pre, s_pp, s_len, s_lo, S, Hk, has_next ? item + nwaves : item);
     int pid_n = fetch_pages(a, nxt, has_next);
     // A full wait (never too weak): the loop then finds pid and pid_n
     // resolved on entry as it does on every later iteration, and its
@@ -590,24 +627,27 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         // The item after next: geometry and table entries now.
         const int next2 = item + 2 * nwaves;
         const bool has_next2 = next2 < total;
-        const Item nxt2 = resolve_item(s_pre, s_pp, s_len, S, Hk, has_next2 ? next2 : item);
+        const Item nxt2 = resolve_item<KT>(s_pre, s_pp, s_len, s_lo, S, Hk, has_next2 ? next2 : item);
         const int pid_nn = fetch_pages(a, nxt2, has_next2);
 
         const int s = cur.s, j = cur.j, kh = cur.kh, C = cur.C, t0 = cur.t0, t1 = cur.t1;
         const int npg = cur.npg;
         const int cmr_mod = (C - R) % ppt;
-        const bool badp = lane < npg && (pid < 0 || (int64_t)pid >= a.n_pages);
+        const int f_s = a.kv_floor ? __builtin_amdgcn_readfirstlane(a.kv_floor[s]) : 0;
+        const bool badp = lane < npg && t0 + 16 * lane + 16 > cur.lo &&
+                          (pid < 0 || (int64_t)pid >= a.n_pages);
         const bool bad = __builtin_amdgcn_ballot_w64(badp) != 0;
         const int nt = (t1 - t0 + KT - 1) / KT;
         const int ntp = (nt + NBUF - 1) / NBUF * NBUF;
 
-        int last[NT];
+        int first[NT], last[NT];
         float m[NT], l[NT];
         f32x4 O[NT][G::DB];
 #pragma unroll
         for (int tau = 0; tau < NT; ++tau) {
             const int r = slot_row(n, tau, g, ppt, R, cmr_mod);
             last[tau] = r >= 0 ? C - R + r : -1;
+            first[tau] = r >= 0 ? key_floor(C - R + r, a.window, f_s) : 0;
             m[tau] = neg_inf();
             l[tau] = 0.f;
 #pragma unroll
@@ -621,7 +661,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         auto compute = [&](const Raw<D, FP8>& t, int tile) {
             const int e0 = tile * G::KB;
             const int e1 = G::KB == 2 ? e0 + 1 : e0;
-            compute_tile<D, FP8, NT>(t, qop, last, m, l, O, t0 + KT * tile, kscale(e0),
+            compute_tile<D, FP8, NT, WIN>(t, qop, first, last, m, l, O, t0 + KT * tile, kscale(e0),
                                      kscale(e1), vscale(e0), vscale(e1), kb);
         };
 
@@ -729,8 +769,16 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
             out[e] = 0x7FC0;  // NaN
         return;
     }
+    const int f_s = a.kv_floor ? a.kv_floor[s] : 0;
+    if (f_s < 0 || f_s > C - R) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            out[e] = 0x7FC0;  // NaN
+        return;
+    }
     const int pos = C - R + r;
     const int ns = pos / kChunk + 1;
+    const int jlo = key_floor(pos, a.window, f_s) / kChunk;  // first split the row attends
     const float* ml = a.ml_part + (((int64_t)s * a.max_split * R + r) * H + h) * 2;
     const float* op = a.o_part + (((int64_t)s * a.max_split * R + r) * H + h) * D + lane * E;
     const int64_t mls = (int64_t)R * H * 2, ops = (int64_t)R * H * D;  // per-split strides
@@ -738,9 +786,10 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
     // Splits in groups of 64, lane = split within the group.
     float M = neg_inf();
     bool nan = false;
-    for (int j0 = 0; j0 < ns; j0 += 64) {
+    const int jstart = jlo & ~63;
+    for (int j0 = jstart; j0 < ns; j0 += 64) {
         const int jj = j0 + lane;
-        const float mj = jj < ns ? ml[jj * mls] : neg_inf();
+        const float mj = jj < ns && jj >= jlo ? ml[jj * mls] : neg_inf();
         nan |= mj != mj;
         M = fmaxf(M, mj);
     }
@@ -753,10 +802,10 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
 #pragma unroll
     for (int e = 0; e < E; ++e)
         num[e] = 0.f;
-    for (int j0 = 0; j0 < ns; j0 += 64) {
+    for (int j0 = jstart; j0 < ns; j0 += 64) {
         const int jj = j0 + lane;
         float wj = 0.f, lj = 0.f;
-        if (jj < ns) {
+        if (jj < ns && jj >= jlo) {
             const f32x2 v = *(const f32x2*)(ml + jj * mls);
             wj = v[0] == M ? 1.f : __builtin_amdgcn_exp2f(v[0] - M);
             lj = v[1];
@@ -768,7 +817,7 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
         den = den + dl;
         const int cnt = min(64, ns - j0);
         const float* o0 = op + (int64_t)j0 * ops;
-        int q = 0;
+        int q = max(0, jlo - j0);
         for (; q + 8 <= cnt; q += 8) {
             float ov[8][E];
 #pragma unroll
@@ -796,7 +845,7 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
         out[e] = nan ? (uint16_t)0x7FC0 : (uint16_t)bf16_bits(num[e] / den);
 }
 
-template <int D, bool FP8, int NT>
+template <int D, bool FP8, int NT, bool WIN>
 hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
 {
     static int s_grid[64] = {0};
@@ -810,7 +859,8 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess)
             return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<D, FP8, NT>, 256, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<D, FP8, NT, WIN>, 256,
+                                                         0);
         if (e != hipSuccess)
             return e;
         grid_cap = cus * (per > 0 ? per : 1);
@@ -826,7 +876,8 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
         blocks = 1;
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, stream);
-    hipLaunchKernelGGL((split_kernel<D, FP8, NT>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -838,18 +889,28 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int D, bool FP8>
-hipError_t launch_nt(const SplitArgs& a, int nt, hipStream_t stream)
+template <int D, bool FP8, bool WIN>
+hipError_t launch_nt_w(const SplitArgs& a, int nt, hipStream_t stream)
 {
     switch (nt) {
-    case 1: return launch_split_t<D, FP8, 1>(a, stream);
-    case 2: return launch_split_t<D, FP8, 2>(a, stream);
+    case 1: return launch_split_t<D, FP8, 1, WIN>(a, stream);
+    case 2: return launch_split_t<D, FP8, 2, WIN>(a, stream);
     case 4:
         if constexpr (D <= 128)
-            return launch_split_t<D, FP8, 4>(a, stream);
+            return launch_split_t<D, FP8, 4, WIN>(a, stream);
         return hipErrorNotSupported;
     default: return hipErrorNotSupported;
     }
+}
+
+// Calls with a window or a floor run instantiations that also compare each
+// key with the row's first key; the others keep the single compare.
+template <int D, bool FP8>
+hipError_t launch_nt(const SplitArgs& a, int nt, hipStream_t stream)
+{
+    if (a.window > 0 || a.kv_floor)
+        return launch_nt_w<D, FP8, true>(a, nt, stream);
+    return launch_nt_w<D, FP8, false>(a, nt, stream);
 }
 
 }  // namespace

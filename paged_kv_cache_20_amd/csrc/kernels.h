@@ -38,6 +38,11 @@ struct SplitArgs {
     int32_t max_split;
     hipEvent_t ev_start, ev_stop;  // optional timing pair around the split kernel
     int32_t max_blocks;            // grid bound for the split kernel; 0 = fill the device
+    // Lower bound on the keys a row attends: row at position p reads keys
+    // max(kv_floor[s], p - window + 1) .. p (window 0: no window; kv_floor
+    // null: floor 0).  A floor outside 0 .. C - rows gives NaN rows.
+    int32_t window;
+    const int32_t* kv_floor;
 };
 
 // Decode (rows = 1) and verify (rows = 8): split kernel + fixed-order combine.
@@ -84,6 +89,11 @@ struct PrefillArgs {
     int32_t n_var;              // sequences of the launch
     int32_t max_q_len;          // bound on any sequence's rows (sizes the grid)
     int32_t n_tok;              // token rows of q and out
+    // Lower bound on the keys a row attends (one-sequence launch only): row
+    // at position p reads keys max(kv_floor, p - window + 1) .. p; window 0
+    // means no window.  0 <= kv_floor <= the first row's position.
+    int32_t window;
+    int32_t kv_floor;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

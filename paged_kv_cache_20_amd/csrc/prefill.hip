@@ -115,16 +115,18 @@ struct PGeo {
 
 struct Blk {
     int C, kh, Hk;
+    int lo;  // first key any row of the workgroup attends (window / floor)
     int64_t n_pages;
     const int32_t* bt;
 };
 
 // Block-table entry of the page holding keys key0 .. key0 + 15 (raw, not yet
-// checked); -1 past the context.  Issued tiles ahead so its latency hides
-// behind compute.
+// checked); -1 past the context and for a page wholly below the first key
+// attended (a runtime floor may have released it).  Issued tiles ahead so
+// its latency hides behind compute.
 __device__ __forceinline__ int fetch_page(const Blk& b, int key0)
 {
-    return key0 < b.C ? b.bt[key0 >> 4] : -1;
+    return key0 < b.C && key0 + 16 > b.lo ? b.bt[key0 >> 4] : -1;
 }
 
 // That page and the number of its rows below the context; page -1 (and 0
@@ -136,7 +138,7 @@ __device__ __forceinline__ void resolve_page(const Blk& b, int key0, int raw, in
     const int p = __builtin_amdgcn_readfirstlane(raw);
     pg = -1;
     rows = 0;
-    if (key0 < b.C) {
+    if (key0 < b.C && key0 + 16 > b.lo) {
         if (p < 0 || (int64_t)p >= b.n_pages) {
             *bad = 1;
         } else {
@@ -300,9 +302,15 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
     const int maxpos = base_pos + rlast;  // last key any row here needs
     const int minpos = base_pos + pb * BP;
     const int nt = (maxpos + kKT) / kKT;
+    // First key a row at position p attends: its sliding window and the
+    // sequence's floor, whichever is later.
+    auto key_floor = [&](int p) { return max(a.kv_floor, a.window > 0 ? p - a.window + 1 : 0); };
+    const int lo_min = key_floor(minpos), lo_max = key_floor(maxpos);
+    b.lo = lo_min;
+    const int ts = lo_min / kKT;  // first tile with a key to attend
 
     // The lane's query row in each of the wave's row tiles (row n of 16).
-    int row[RT], head[RT], pos[RT];
+    int row[RT], head[RT], pos[RT], klo[RT];
     u32x4 qop[RT][G::KSTEPS];  // Q^T operand: d = 32 st + 8 kb + 0..7
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -312,6 +320,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         head[rt] = kh * g + hg;
         const bool valid = row[rt] < n_rows;
         pos[rt] = valid ? base_pos + row[rt] : -1;
+        klo[rt] = key_floor(pos[rt]);
         const uint16_t* q =
             (const uint16_t*)a.q + ((tok0 + (valid ? row[rt] : 0)) * H + head[rt]) * D;
 #pragma unroll
@@ -395,25 +404,26 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
     // whose first key is tile0 + wk.
     const int wk = ((wave * G::KPW) >> 4) * 16;
     Staged<G> stk, stv;
-    int rawv = fetch_page(b, wk);        // block-table entries of the next V
-    int rawk = fetch_page(b, kKT + wk);  // and K tiles to load
+    const int k0 = ts * kKT;
+    int rawv = fetch_page(b, k0 + wk);        // block-table entries of the next V
+    int rawk = fetch_page(b, k0 + kKT + wk);  // and K tiles to load
     if constexpr (STG) {
-        stage_load<G>(stk, kp, a.k_scale, b, wk, wave, lane, rawv, &bad);
+        stage_load<G>(stk, kp, a.k_scale, b, k0 + wk, wave, lane, rawv, &bad);
         stage_store<G>(stk, s_k0, s_ksc[0], wave, lane);
-        stage_load<G>(stv, vp, a.v_scale, b, wk, wave, lane, rawv, &bad);
+        stage_load<G>(stv, vp, a.v_scale, b, k0 + wk, wave, lane, rawv, &bad);
         stage_store<G>(stv, s_v0, s_vsc[0], wave, lane);
-        if (nt > 1) {
-            stage_load<G>(stk, kp, a.k_scale, b, kKT + wk, wave, lane, rawk, &bad);
+        if (nt > ts + 1) {
+            stage_load<G>(stk, kp, a.k_scale, b, k0 + kKT + wk, wave, lane, rawk, &bad);
             stage_store<G>(stk, s_k1, s_ksc[1], wave, lane);
         }
     } else {
-        issue_direct<G>(s_k0, kp, b, wk, wave, loff, rawv, &bad);
-        issue_direct<G>(s_v0, vp, b, wk, wave, loff, rawv, &bad);
-        if (nt > 1)
-            issue_direct<G>(s_k1, kp, b, kKT + wk, wave, loff, rawk, &bad);
+        issue_direct<G>(s_k0, kp, b, k0 + wk, wave, loff, rawv, &bad);
+        issue_direct<G>(s_v0, vp, b, k0 + wk, wave, loff, rawv, &bad);
+        if (nt > ts + 1)
+            issue_direct<G>(s_k1, kp, b, k0 + kKT + wk, wave, loff, rawk, &bad);
     }
     rawv = rawk;
-    rawk = fetch_page(b, 2 * kKT + wk);
+    rawk = fetch_page(b, k0 + 2 * kKT + wk);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -445,9 +455,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         rawv = rawk;
         rawk = fetch_page(b, tile0 + 3 * kKT + wk);
 
-        // Scale (log2 units) and, on the tile that crosses the causal edge,
-        // mask; then the lane-local max check.
-        const bool diag = tile0 + kKT - 1 > minpos;
+        // Scale (log2 units) and, on a tile that crosses the causal edge or
+        // the first key of some row, mask; then the lane-local max check.
+        const bool diag = tile0 + kKT - 1 > minpos || tile0 < lo_max;
         float sx[4];  // factor applied to cur in the exponent
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq)
@@ -461,9 +471,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
                 for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        const float v = tile0 + 16 * kq + 4 * kb + x > pos[rt]
-                                            ? neg_inf()
-                                            : cur[rt][kq][x] * sx[kq];
+                        const int key = tile0 + 16 * kq + 4 * kb + x;
+                        const float v = key > pos[rt] || key < klo[rt] ? neg_inf()
+                                                                        : cur[rt][kq][x] * sx[kq];
                         cur[rt][kq][x] = v;
                         mx = fmaxf(mx, v);
                     }
@@ -578,7 +588,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         }
         __syncthreads();
     };
-    for (int t = 0; t < nt; t += 2) {
+    for (int t = ts; t < nt; t += 2) {
         tile_body(t, s_k1, s_v0, s_k0, s_v1, s_ksc[1], s_vsc[0], s_ksc[0], s_vsc[1], sa, ka, sb,
                   kb4);
         if (t + 1 < nt)

@@ -114,6 +114,34 @@ def test_verify_width_rejects_unserved_group(pa):
     assert e.value.code == pa.ATTN_E_UNSUPPORTED
 
 
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(rows=0), -2, "zero rows"), (dict(rows=9), -3, "rows 9"),
+    (dict(window=-1), -5, "window -1"), (dict(q=None), -1, "q is NULL"),
+])
+def test_decode_window_host_checks(pa, over, code, needle):
+    args = decode_args(rows=1, window=0, kv_floor=None)
+    args.update(over)
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_decode_window(**args)
+    assert e.value.code == code
+    assert needle in str(e.value)
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(window=-2), -5, "window -2"),
+    (dict(kv_floor=-1), -5, "kv_floor -1"),
+    (dict(kv_floor=28673), -5, "kv_floor 28673"),
+    (dict(n_rows=0), -2, "zero rows"),
+])
+def test_prefill_window_host_checks(pa, over, code, needle):
+    args = prefill_args(window=0, kv_floor=0)
+    args.update(over)
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_prefill_window(**args)
+    assert e.value.code == code
+    assert needle in str(e.value)
+
+
 def test_verify_rejects_unserved_group(pa):
     # 16 heads per kv head at head_dim 256: 8 tiles x 256 > 512 accumulator columns
     with pytest.raises(pa.AttnError) as e:
