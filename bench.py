@@ -300,6 +300,46 @@ class Bench:
                 "note": "medians of whole-call spans (every kernel of the call) by events on "
                         "the call's stream"}
 
+    def time_window(self, window=4096, steps=20, warmup=5):
+        """The 256-sequence fp8 decode step with a sliding window: split
+        kernel time (library kernel timer) and the bytes of the keys in
+        each row's window."""
+        torch, pa = self.torch, self.pa
+        st = self.setup_split("decode_256seq_fp8")
+        w, inp = st["w"], st["inp"]
+
+        def call():
+            pa.attn_paged_decode_window(inp.q, 1, st["k"], st["v"], st["ks"], st["vs"],
+                                        inp.n_pages, inp.table, w.max_pages, inp.lengths,
+                                        w.n_seq, window, None, w.n_head, w.n_head_kv,
+                                        w.head_dim, 16, st["kv"], st["out"], st["ws"], st["wsb"])
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
+        for i in range(steps):
+            pa.attn_set_kernel_timer(evs[i][0], evs[i][1])
+            call()
+        torch.cuda.synchronize()
+        kern = sorted(self.ev.elapsed_ms(a, b) for a, b in evs)
+        for a, b in evs:
+            self.ev.destroy(a)
+            self.ev.destroy(b)
+        us = kern[len(kern) // 2] * 1e3
+        # keys in the window of each row; pages (scales, table) from the first
+        # page holding one of them
+        b = 1
+        tot = 0
+        for c in st["lengths_host"]:
+            lo = max(0, c - window)
+            pages = -(-c // 16) - lo // 16
+            tot += (c - lo) * w.n_head_kv * w.head_dim * 2 * b + pages * 4 + \
+                pages * w.n_head_kv * 2 * 4
+        tot += w.n_seq * w.n_head * w.head_dim * 2 + 4 * w.n_seq
+        return {"window": window, "kernel_median_us": round(us, 2), "bytes": tot,
+                "kernel_gbs": round(tot / (us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(tot / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
     def time_widths(self, widths=(1, 2, 4, 8), steps=20, warmup=5):
         """Rounds of several widths over the 32-sequence verify cache (d 256,
         bf16, 4,104 tokens each): split-kernel time per width (HIP events
@@ -517,6 +557,13 @@ def main():
                 sec[other] = {"error": str(e)[:200]}
             torch.cuda.empty_cache()
             log("[bench] secondary done", other, sec[other])
+        log("[bench] secondary windowed decode")
+        try:
+            sec["decode_256seq_fp8_window4096"] = b.time_window()
+        except Exception as e:  # report, keep the headline
+            sec["decode_256seq_fp8_window4096"] = {"error": str(e)[:200]}
+        torch.cuda.empty_cache()
+        log("[bench] secondary done", sec["decode_256seq_fp8_window4096"])
         log("[bench] secondary verify widths")
         try:
             sec["verify_32seq_widths_1_2_4_8"] = b.time_widths()
