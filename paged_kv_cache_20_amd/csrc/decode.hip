@@ -390,7 +390,8 @@ __device__ __forceinline__ bool ctx_ok(int C, int R, int64_t cap) { return C >= 
 // A work item resolved to its sequence, split and kv head.
 struct Item {
     int s, j, kh, C, t0, t1, npg;
-    int lo;  // first key the item's rows may attend (window / floor), <= t0 + KT - 1
+    int lo;    // first key the item's rows may attend (window / floor), <= t0 + KT - 1
+    int tau0;  // first slot tile of the call that the item covers
 };
 
 // First key position row `pos` attends: its sliding window (window > 0)
@@ -404,10 +405,15 @@ __device__ __forceinline__ int key_floor(int pos, int window, int floor_s)
 // partial last splits (sequence, kv head): a wave's later items are the
 // short ones, so the grid's last round is short.  s_pre / s_pp: exclusive
 // prefixes over sequences of their full / partial items.
-template <int KT>
+template <int KT, int NT>
 __device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, const int* s_len,
-                                             const int* s_lo, int S, int Hk, int item)
+                                             const int* s_lo, int S, int Hk, int slices,
+                                             int item_in)
 {
+    // `slices` consecutive item numbers share one (sequence, split, kv
+    // head) and take NT slot tiles each.
+    const int item = item_in / slices;
+    const int tau0 = (item_in - item * slices) * NT;
     const int nfull = s_pre[S];
     const bool full = item < nfull;
     const int* pre = full ? s_pre : s_pp;
@@ -435,6 +441,7 @@ __device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, 
     it.t0 = base + ((it.lo - base) / KT) * KT;
     it.t1 = min(base + kChunk, it.C);
     it.npg = (it.t1 - it.t0 + 15) >> 4;
+    it.tau0 = __builtin_amdgcn_readfirstlane(tau0);
     return it;
 }
 
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     const int lane = tid & 63, n = lane & 15, kb = lane >> 4;
     // Wave-uniform values are made visibly uniform (scalar registers), so
     // that loop bounds, page ids and buffer resources stay scalar.
-    const int total = __builtin_amdgcn_readfirstlane(s_pre[S] + s_pp[S]);
+    const int total = __builtin_amdgcn_readfirstlane((s_pre[S] + s_pp[S]) * a.slices);
     const int nwaves = gridDim.x * kWaves;
     const float sm_log2 = kLog2e / __builtin_sqrtf((float)D);
     const uint8_t* __restrict__ kp = (const uint8_t*)a.k_pool;
@@ -575,7 +582,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         const int h = I.kh * g + (n % g);
 #pragma unroll
         for (int tau = 0; tau < NT; ++tau) {
-            const int r = slot_row(n, tau, g, ppt, R, cm);
+            const int r = slot_row(n, I.tau0 + tau, g, ppt, R, cm);
             const uint32_t qo = r >= 0 ? (uint32_t)((r * H + h) * D) * 2u : kFar;
 #pragma unroll
             for (int st = 0; st < G::STEPS; ++st)
@@ -605,10 +612,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     // are not computed), so every item starts at ring slot 0.
     // Table entries are fetched two items ahead and held in registers one
     // item ahead, so the ring never waits for them.
-    Item cur = resolve_item<KT>(s_pre, s_pp, s_len, s_lo, S, Hk, item);
+    Item cur = resolve_item<KT, NT>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, item);
     int pid = fetch_pages(a, cur, true);
     bool has_next = item + nwaves < total;
-    Item nxt = resolve_item<KT>(s_pre, s_pp, s_len, s_lo, S, Hk, has_next ? item + nwaves : item);
+    Item nxt = resolve_item<KT, NT>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next ? item + nwaves : item);
     int pid_n = fetch_pages(a, nxt, has_next);
     // A full wait (never too weak): the loop then finds pid and pid_n
     // resolved on entry as it does on every later iteration, and its
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         // The item after next: geometry and table entries now.
         const int next2 = item + 2 * nwaves;
         const bool has_next2 = next2 < total;
-        const Item nxt2 = resolve_item<KT>(s_pre, s_pp, s_len, s_lo, S, Hk, has_next2 ? next2 : item);
+        const Item nxt2 = resolve_item<KT, NT>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next2 ? next2 : item);
         const int pid_nn = fetch_pages(a, nxt2, has_next2);
 
         const int s = cur.s, j = cur.j, kh = cur.kh, C = cur.C, t0 = cur.t0, t1 = cur.t1;
@@ -645,7 +652,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         f32x4 O[NT][G::DB];
 #pragma unroll
         for (int tau = 0; tau < NT; ++tau) {
-            const int r = slot_row(n, tau, g, ppt, R, cmr_mod);
+            const int r = slot_row(n, cur.tau0 + tau, g, ppt, R, cmr_mod);
             last[tau] = r >= 0 ? C - R + r : -1;
             first[tau] = r >= 0 ? key_floor(C - R + r, a.window, f_s) : 0;
             m[tau] = neg_inf();
@@ -705,7 +712,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int slot = 4 * kb + r;
-                const int row = slot_row(slot, tau, g, ppt, R, cmr_mod);
+                const int row = slot_row(slot, cur.tau0 + tau, g, ppt, R, cmr_mod);
                 const int h = kh * g + (slot % g);
                 const uint32_t off =
                     row >= 0 ? (uint32_t)(((row * H + h) * D + n * G::DB) * 4) : kFar;
@@ -718,7 +725,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
                                                            off + 4u * jb, 0, 0);
                 }
             }
-            const int row = slot_row(n, tau, g, ppt, R, cmr_mod);
+            const int row = slot_row(n, cur.tau0 + tau, g, ppt, R, cmr_mod);
             const int h = kh * g + (n % g);
             const uint32_t off = (kb == 0 && row >= 0) ? (uint32_t)((row * H + h) * 8) : kFar;
             const f32x2 v = bad ? f32x2{qnan, qnan} : f32x2{m[tau], l[tau]};
@@ -866,7 +873,7 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
         grid_cap = cus * (per > 0 ? per : 1);
     }
     const int Hk = a.n_head_kv;
-    const int64_t upper = (int64_t)a.n_seq * a.max_split * Hk;  // items, at most
+    const int64_t upper = (int64_t)a.n_seq * a.max_split * Hk * a.slices;  // items, at most
     int64_t blocks = (upper + kWaves - 1) / kWaves;
     if (blocks > grid_cap)
         blocks = grid_cap;
@@ -889,15 +896,30 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int D, bool FP8, bool WIN>
-hipError_t launch_nt_w(const SplitArgs& a, int nt, hipStream_t stream)
+// Slot tiles per work item for a call needing `nt` tiles: the rest of the
+// call's tiles go to sibling items (consecutive numbers, the same keys, so
+// the second read of a tile comes from L2).  A row's arithmetic is the same
+// in any tile of any instantiation, so this changes no bit of the output.
+// Measured: at head_dim 128 two tiles per item beat one (fp8, 8 rows x 4
+// heads) and four (bf16, 8 rows x 8 heads: 514 -> 299 us); at head_dim 256
+// one tile per item equals two.
+template <int D>
+int kernel_tiles(int nt)
 {
-    switch (nt) {
+    return D == 256 ? 1 : (nt < 2 ? nt : 2);
+}
+
+template <int D, bool FP8, bool WIN>
+hipError_t launch_nt_w(const SplitArgs& a0, int nt, hipStream_t stream)
+{
+    const int ntk = kernel_tiles<D>(nt);
+    SplitArgs a = a0;
+    a.slices = nt / ntk;
+    switch (ntk) {
     case 1: return launch_split_t<D, FP8, 1, WIN>(a, stream);
-    case 2: return launch_split_t<D, FP8, 2, WIN>(a, stream);
-    case 4:
+    case 2:
         if constexpr (D <= 128)
-            return launch_split_t<D, FP8, 4, WIN>(a, stream);
+            return launch_split_t<D, FP8, 2, WIN>(a, stream);
         return hipErrorNotSupported;
     default: return hipErrorNotSupported;
     }

@@ -43,6 +43,7 @@ struct SplitArgs {
     // null: floor 0).  A floor outside 0 .. C - rows gives NaN rows.
     int32_t window;
     const int32_t* kv_floor;
+    int32_t slices;  // work items per (sequence, split, kv head); set by the launcher
 };
 
 // Decode (rows = 1) and verify (rows = 8): split kernel + fixed-order combine.
