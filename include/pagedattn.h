@@ -341,6 +341,25 @@ int attn_check_block_table_host(const int32_t* block_table_host, const int32_t* 
                                 int32_t n_seq, int32_t max_pages_per_seq, int32_t page_size,
                                 int64_t n_pages);
 
+/*
+ * attn_check_device -- checked mode on the device, for callers without host
+ * copies ("kern manifest v7" schema, $defs.Domain: out-of-domain inputs are
+ * rejected; $defs.Fill "error": a one-word error flag read after the call).
+ * Enqueues a check of what a call with these arguments would read: every
+ * ctx_lens[s] in rows .. max_pages_per_seq * page_size, and every block-table
+ * entry of a page holding a key some row attends (pages wholly below the
+ * first key of the first row -- window and kv_floor as for
+ * attn_paged_decode_window, 0 / NULL for none -- are skipped) in
+ * [0, n_pages).  *err_word (device int64) becomes -1 when all hold, else
+ * s * (max_pages_per_seq + 1) + e + 1 for the first failure in (sequence,
+ * entry) order, e = -1 naming the length.  Read it after the stream has
+ * passed the call.
+ */
+int attn_check_device(const int32_t* block_table, const int32_t* ctx_lens,
+                      const int32_t* kv_floor, int32_t window, int32_t n_seq, int32_t rows,
+                      int32_t max_pages_per_seq, int32_t page_size, int64_t n_pages,
+                      int64_t* err_word, hipStream_t stream);
+
 /* Message of the last failing call on this thread ("" after a success). */
 const char* attn_last_error(void);
 

@@ -35,7 +35,8 @@ EXPORTS = [
     "attn_paged_decode", "attn_paged_verify", "attn_paged_verify_width", "attn_paged_prefill",
     "attn_paged_mixed", "attn_paged_decode_window", "attn_paged_prefill_window",
     "attn_kv_append", "attn_block_table_build", "attn_paged_workspace_bytes", "attn_caps",
-    "attn_check_lengths_host", "attn_check_block_table_host", "attn_last_error",
+    "attn_check_lengths_host", "attn_check_block_table_host", "attn_check_device",
+    "attn_last_error",
     "attn_set_kernel_timer", "attn_set_max_workgroups",
 ]
 
@@ -92,6 +93,8 @@ _lib.attn_check_lengths_host.argtypes = [_P, _I32, _I32, _I32, _I32]
 _lib.attn_check_lengths_host.restype = ctypes.c_int
 _lib.attn_check_block_table_host.argtypes = [_P, _P, _I32, _I32, _I32, _I64]
 _lib.attn_check_block_table_host.restype = ctypes.c_int
+_lib.attn_check_device.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I64, _P, _P]
+_lib.attn_check_device.restype = ctypes.c_int
 _lib.attn_last_error.argtypes = []
 _lib.attn_last_error.restype = ctypes.c_char_p
 _lib.attn_set_kernel_timer.argtypes = [_P, _P]
@@ -196,6 +199,13 @@ def attn_paged_prefill_window(q, n_rows, k_pool, v_pool, k_scale, v_scale, n_pag
         _dp(block_table), max_pages_per_seq, ctx_len, window, kv_floor, n_head, n_head_kv,
         head_dim, page_size, kv_dtype, _dp(out), _dp(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def attn_check_device(block_table, ctx_lens, kv_floor, window, n_seq, rows, max_pages_per_seq,
+                      page_size, n_pages, err_word, stream=None):
+    return _check(_lib.attn_check_device(
+        _dp(block_table), _dp(ctx_lens), _dp(kv_floor), window, n_seq, rows, max_pages_per_seq,
+        page_size, n_pages, _dp(err_word), _stream(stream)))
 
 
 def attn_paged_mixed(q, n_tok, cu_seqlens, n_seq, n_seq_decode, max_q_len, k_pool, v_pool,

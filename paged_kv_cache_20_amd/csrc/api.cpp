@@ -199,6 +199,37 @@ extern "C" {
 
 const char* attn_last_error(void) { return t_err; }
 
+int attn_check_device(const int32_t* block_table, const int32_t* ctx_lens,
+                      const int32_t* kv_floor, int32_t window, int32_t n_seq, int32_t rows,
+                      int32_t max_pages_per_seq, int32_t page_size, int64_t n_pages,
+                      int64_t* err_word, hipStream_t stream)
+{
+    const char* fn = "attn_check_device";
+    if (!block_table || !ctx_lens || !err_word)
+        return fail(ATTN_E_ARG, "%s: block_table, ctx_lens and err_word must not be NULL", fn);
+    if (n_seq <= 0 || rows <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero sequences or rows is not a call (%d, %d)", fn, n_seq,
+                    rows);
+    if (max_pages_per_seq <= 0 || n_pages <= 0)
+        return fail(ATTN_E_SHAPE, "%s: max_pages_per_seq and n_pages must be positive", fn);
+    if (page_size != ATTN_PAGE_SIZE)
+        return fail(ATTN_E_UNSUPPORTED, "%s: page_size %d not served", fn, page_size);
+    if (window < 0)
+        return fail(ATTN_E_RANGE, "%s: window %d is negative", fn, window);
+    pa::CheckArgs a;
+    a.block_table = block_table;
+    a.ctx_lens = ctx_lens;
+    a.kv_floor = kv_floor;
+    a.window = window;
+    a.n_seq = n_seq;
+    a.rows = rows;
+    a.max_pages = max_pages_per_seq;
+    a.page_size = page_size;
+    a.n_pages = n_pages;
+    a.err = err_word;
+    return from_hip(pa::launch_check(a, stream), fn);
+}
+
 void attn_set_kernel_timer(hipEvent_t start, hipEvent_t stop)
 {
     t_ev_start = start;

@@ -98,4 +98,15 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+struct CheckArgs {
+    const int32_t* block_table;
+    const int32_t* ctx_lens;
+    const int32_t* kv_floor;  // or null
+    int32_t window;           // 0: none
+    int32_t n_seq, rows, max_pages, page_size;
+    int64_t n_pages;
+    int64_t* err;  // -1, or s * (max_pages + 1) + entry + 1 (entry -1: the length)
+};
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
+
 }  // namespace pa

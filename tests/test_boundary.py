@@ -142,6 +142,25 @@ def test_prefill_window_host_checks(pa, over, code, needle):
     assert needle in str(e.value)
 
 
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(block_table=None), -1, "must not be NULL"),
+    (dict(err_word=None), -1, "must not be NULL"),
+    (dict(n_seq=0), -2, "zero sequences"),
+    (dict(rows=0), -2, "zero sequences or rows"),
+    (dict(n_pages=0), -2, "n_pages"),
+    (dict(page_size=8), -3, "page_size 8"),
+    (dict(window=-4), -5, "window -4"),
+])
+def test_check_device_host_checks(pa, over, code, needle):
+    args = dict(block_table=FAKE, ctx_lens=FAKE, kv_floor=None, window=0, n_seq=4, rows=1,
+                max_pages_per_seq=32, page_size=16, n_pages=64, err_word=FAKE, stream=0)
+    args.update(over)
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_check_device(**args)
+    assert e.value.code == code
+    assert needle in str(e.value)
+
+
 def test_verify_rejects_unserved_group(pa):
     # 16 heads per kv head at head_dim 256: 8 tiles x 256 > 512 accumulator columns
     with pytest.raises(pa.AttnError) as e:
