@@ -160,9 +160,13 @@ class Bench:
         self.torch, self.pa, self.synth = torch, pa, synth
         self.ev = HipEvents()
 
-    def setup_split(self, name):
+    def setup_split(self, name, spare_pages=0):
         torch, pa, synth = self.torch, self.pa, self.synth
         w = synth.WORKLOADS[name]
+        if spare_pages:
+            need = sum(-(-c // 16) for c in synth.draw_lengths(
+                w, torch.Generator(device="cpu").manual_seed(w.seed)).tolist())
+            w = synth.scaled(w, pool_pages=need + w.n_seq + spare_pages)
         inp = synth.draw(w, "cuda")
         k, v, ks, vs = synth.poison_pools(inp.n_pages, w, "cuda")
         kv = pa.KV_FP8_E4M3 if w.kv_fp8 else pa.KV_BF16
@@ -376,6 +380,58 @@ class Bench:
                                   "hbm_frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         return res
 
+    def time_tree(self, width=8, steps=20, warmup=5):
+        """A tree-shaped round of 8 rows per sequence (each row's parent drawn
+        at random among the earlier rows, seed 1008) over the 32-sequence
+        verify cache: the whole call (branch staging, split kernel, combine)
+        and its split kernel alone, medians of HIP events."""
+        import numpy as np
+        torch, pa = self.torch, self.pa
+        st = self.setup_split("verify_32seq_8rows", spare_pages=2 * 32 * width)
+        w, inp = st["w"], st["inp"]
+        S = w.n_seq
+        rng = np.random.default_rng(1008)
+        masks = np.zeros((S, width), np.int32)
+        for s in range(S):
+            for r in range(width):
+                par = int(rng.integers(-1, r))
+                masks[s, r] = (1 << r) | (masks[s, par] if par >= 0 else 0)
+        used = set(inp.table.cpu().numpy().ravel().tolist())
+        free = [p for p in range(inp.n_pages) if p not in used][:2 * S * width]
+        scratch = torch.tensor(free, dtype=torch.int32, device="cuda")
+        mask_d = torch.from_numpy(masks).cuda()
+        wsb = pa.attn_paged_workspace_bytes(4, S, w.max_pages, w.n_head, w.head_dim)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        q = inp.q[:, :width].contiguous()
+        out = torch.empty_like(q)
+
+        def call():
+            pa.attn_paged_verify_tree(q, st["k"], st["v"], st["ks"], st["vs"], inp.n_pages,
+                                      inp.table, w.max_pages, inp.lengths, S, width, mask_d,
+                                      scratch, w.n_head, w.n_head_kv, w.head_dim, 16, st["kv"],
+                                      out, ws, wsb)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        kev = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i in range(steps):
+            pa.attn_set_kernel_timer(kev[i][0], kev[i][1])
+            cev[i][0].record()
+            call()
+            cev[i][1].record()
+        torch.cuda.synchronize()
+        kern = sorted(self.ev.elapsed_ms(a, b) for a, b in kev)
+        whole = sorted(a.elapsed_time(b) for a, b in cev)
+        for a, b in kev:
+            self.ev.destroy(a)
+            self.ev.destroy(b)
+        depth = int(sum(bin(int(m)).count("1") for m in masks.ravel()))
+        return {"call_median_us": round(whole[len(whole) // 2] * 1e3, 2),
+                "split_kernel_median_us": round(kern[len(kern) // 2] * 1e3, 2),
+                "rows": S * width, "mean_branch_depth": round(depth / (S * width), 3)}
+
     def time_prefill(self, st, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
@@ -571,6 +627,13 @@ def main():
             sec["verify_32seq_widths_1_2_4_8"] = {"error": str(e)[:200]}
         torch.cuda.empty_cache()
         log("[bench] secondary done", sec["verify_32seq_widths_1_2_4_8"])
+        log("[bench] secondary tree round")
+        try:
+            sec["verify_32seq_tree8"] = b.time_tree()
+        except Exception as e:  # report, keep the headline
+            sec["verify_32seq_tree8"] = {"error": str(e)[:200]}
+        torch.cuda.empty_cache()
+        log("[bench] secondary done", sec["verify_32seq_tree8"])
         log("[bench] secondary mixed_256dec_fp8_plus_2048chunk")
         try:
             sec["mixed_256dec_fp8_plus_2048chunk"] = b.time_mixed()

@@ -180,6 +180,43 @@ int attn_paged_verify_width(const void* q, const void* k_pool, const void* v_poo
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_paged_verify_tree -- a speculative round of `width` rows shaped as a
+ * tree ("Radiance Architecture Plugins -- declaring a model", section
+ * "Declare: drafters, encoders, generators": a drafter may propose a tree;
+ * "TandemLLM -- Adding a model", section "The adapter path in ten steps":
+ * rounds replayed as trees must match the recorded decode bit for bit).
+ *
+ *   q, out         bf16 [n_seq][width][n_head][head_dim]; the round's rows
+ *                  are in the cache at positions C0 .. C0 + width - 1,
+ *                  C0 = ctx_lens[s] - width (attn_kv_append first)
+ *   tree_mask      int32 [n_seq][width], DEVICE: bit j of row r's entry set
+ *                  = row r attends round row j.  A row names itself and only
+ *                  earlier rows (its ancestors); anything else gives NaN rows.
+ *   scratch_pages  int32 [n_seq][width][2], DEVICE: pool pages the call may
+ *                  overwrite (two per row, distinct, unused by any sequence);
+ *                  the branch views are built there.  With an fp8 pool their
+ *                  scales are overwritten too.
+ *   k_pool, v_pool, k_scale, v_scale  writable (scratch pages only).
+ *   workspace      attn_paged_workspace_bytes(4, n_seq, ...)
+ * Row r attends keys 0 .. C0 - 1 and the round rows its mask names, in row
+ * order; its result equals, bit for bit, attn_paged_decode of the same row
+ * over a cache holding the context followed by those rows at positions C0,
+ * C0 + 1, ... (its branch).  A chain mask (row r names 0 .. r) gives the
+ * attn_paged_verify_width rows.  Bytes are copied into the views, never
+ * re-quantised, so with an fp8 pool a round must lie inside one page (one
+ * scale); rows of a round that does not get NaN.  Needs n_seq * width <=
+ * 4096 and at most 16 query heads per kv head.  Each row reads its whole
+ * context (width times the bytes of a chain round).
+ */
+int attn_paged_verify_tree(const void* q, void* k_pool, void* v_pool, float* k_scale,
+                           float* v_scale, int64_t n_pages, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t n_seq,
+                           int32_t width, const int32_t* tree_mask, const int32_t* scratch_pages,
+                           int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+                           int32_t page_size, attn_kv_dtype kv_dtype, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_paged_prefill -- a chunk of n_rows new rows of ONE sequence over its
  * cached context ("kern manifest v7" schema, $defs.Batch: rows given by the
  * chunk, one sequence; `context` is the cached rows it expands over).
@@ -322,7 +359,7 @@ int attn_block_table_build(int32_t n_seq, const int32_t* ctx_lens_host, int32_t 
                            int32_t* block_table_host, int32_t* slot_mapping_host);
 
 /* op: 0 decode, 1 verify, 2 prefill, 3 mixed (n_seq = the step's
-   n_seq_decode).  Bytes of device workspace the call needs; 0 for an
+   n_seq_decode), 4 tree round (any width).  Bytes of device workspace the call needs; 0 for an
    unsupported combination. */
 size_t attn_paged_workspace_bytes(int op, int32_t n_seq, int32_t max_pages_per_seq,
                                   int32_t n_head, int32_t head_dim);

@@ -32,7 +32,8 @@ ATTN_E_RANGE = -5
 ATTN_E_DEVICE = -6
 
 EXPORTS = [
-    "attn_paged_decode", "attn_paged_verify", "attn_paged_verify_width", "attn_paged_prefill",
+    "attn_paged_decode", "attn_paged_verify", "attn_paged_verify_width",
+    "attn_paged_verify_tree", "attn_paged_prefill",
     "attn_paged_mixed", "attn_paged_decode_window", "attn_paged_prefill_window",
     "attn_kv_append", "attn_block_table_build", "attn_paged_workspace_bytes", "attn_caps",
     "attn_check_lengths_host", "attn_check_block_table_host", "attn_check_device",
@@ -67,6 +68,9 @@ _lib.attn_paged_verify.restype = ctypes.c_int
 _lib.attn_paged_verify_width.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                          _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]
 _lib.attn_paged_verify_width.restype = ctypes.c_int
+_lib.attn_paged_verify_tree.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P,
+                                        _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]
+_lib.attn_paged_verify_tree.restype = ctypes.c_int
 _lib.attn_paged_prefill.argtypes = [_P, _I32, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32, _I32,
                                     _I32, _I32, _I32, _P, _P, _SZ, _P]
 _lib.attn_paged_prefill.restype = ctypes.c_int
@@ -206,6 +210,17 @@ def attn_check_device(block_table, ctx_lens, kv_floor, window, n_seq, rows, max_
     return _check(_lib.attn_check_device(
         _dp(block_table), _dp(ctx_lens), _dp(kv_floor), window, n_seq, rows, max_pages_per_seq,
         page_size, n_pages, _dp(err_word), _stream(stream)))
+
+
+def attn_paged_verify_tree(q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                           max_pages_per_seq, ctx_lens, n_seq, width, tree_mask, scratch_pages,
+                           n_head, n_head_kv, head_dim, page_size, kv_dtype, out, workspace=None,
+                           workspace_bytes=0, stream=None):
+    return _check(_lib.attn_paged_verify_tree(
+        _dp(q), _dp(k_pool), _dp(v_pool), _dp(k_scale), _dp(v_scale), n_pages, _dp(block_table),
+        max_pages_per_seq, _dp(ctx_lens), n_seq, width, _dp(tree_mask), _dp(scratch_pages),
+        n_head, n_head_kv, head_dim, page_size, kv_dtype, _dp(out), _dp(workspace),
+        workspace_bytes, _stream(stream)))
 
 
 def attn_paged_mixed(q, n_tok, cu_seqlens, n_seq, n_seq_decode, max_q_len, k_pool, v_pool,

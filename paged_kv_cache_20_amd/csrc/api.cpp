@@ -127,6 +127,22 @@ size_t split_ws_bytes(int32_t rows, int32_t n_seq, int32_t max_pages, int32_t n_
     return (size_t)(o_bytes + rec * 2 * 4);
 }
 
+// Workspace of a tree round: the branch views' table rows and lengths, then
+// the split-K partials of n_seq * 8 one-row sequences.
+size_t tree_ws_bytes(int32_t n_seq, int32_t max_pages, int32_t n_head, int32_t head_dim,
+                            size_t* off_lens, size_t* off_split)
+{
+    const int64_t nv = (int64_t)n_seq * ATTN_VERIFY_ROWS;
+    const size_t tb = (size_t)((nv * max_pages * 4 + 255) / 256 * 256);
+    const size_t lb = (size_t)((nv * 4 + 255) / 256 * 256);
+    if (off_lens)
+        *off_lens = tb;
+    if (off_split)
+        *off_split = tb + lb;
+    return tb + lb + split_ws_bytes(1, (int32_t)nv, max_pages, n_head, head_dim);
+}
+
+
 int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
                const void* v_pool, const float* k_scale, const float* v_scale, int64_t n_pages,
                const int32_t* block_table, int32_t max_pages, const int32_t* ctx_lens,
@@ -262,6 +278,7 @@ size_t attn_paged_workspace_bytes(int op, int32_t n_seq, int32_t max_pages_per_s
     case 1: return split_ws_bytes(ATTN_VERIFY_ROWS, n_seq, max_pages_per_seq, n_head, head_dim);
     case 2: return 0;
     case 3: return split_ws_bytes(1, n_seq, max_pages_per_seq, n_head, head_dim);
+    case 4: return tree_ws_bytes(n_seq, max_pages_per_seq, n_head, head_dim, nullptr, nullptr);
     default: return 0;
     }
 }
@@ -362,6 +379,70 @@ static int prefill_call(const char* fn, const void* q, int32_t n_rows, const voi
     a.window = window;
     a.kv_floor = kv_floor;
     return from_hip(pa::launch_prefill(a, stream), fn);
+}
+
+int attn_paged_verify_tree(const void* q, void* k_pool, void* v_pool, float* k_scale,
+                           float* v_scale, int64_t n_pages, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* ctx_lens, int32_t n_seq,
+                           int32_t width, const int32_t* tree_mask, const int32_t* scratch_pages,
+                           int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+                           int32_t page_size, attn_kv_dtype kv_dtype, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char* fn = "attn_paged_verify_tree";
+    int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                          max_pages_per_seq, n_head, n_head_kv, head_dim, page_size, kv_dtype,
+                          out);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!ctx_lens || !tree_mask || !scratch_pages)
+        return fail(ATTN_E_ARG, "%s: ctx_lens, tree_mask and scratch_pages must not be NULL",
+                    fn);
+    if (width <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (width = %d)", fn, width);
+    if (width > ATTN_VERIFY_ROWS)
+        return fail(ATTN_E_UNSUPPORTED, "%s: width %d above %d", fn, width, ATTN_VERIFY_ROWS);
+    if (n_seq <= 0)
+        return fail(ATTN_E_SHAPE, "%s: zero sequences is not a call (n_seq = %d)", fn, n_seq);
+    if ((int64_t)n_seq * width > pa::kMaxSeq)
+        return fail(ATTN_E_UNSUPPORTED, "%s: n_seq * width %lld above %d", fn,
+                    (long long)n_seq * width, pa::kMaxSeq);
+    if (n_head / n_head_kv > 16)
+        return fail(ATTN_E_UNSUPPORTED, "%s: %d query heads per kv head (at most 16)", fn,
+                    n_head / n_head_kv);
+    size_t off_lens = 0, off_split = 0;
+    const size_t need =
+        tree_ws_bytes(n_seq, max_pages_per_seq, n_head, head_dim, &off_lens, &off_split);
+    rc = check_workspace(fn, workspace, workspace_bytes, need);
+    if (rc != ATTN_OK)
+        return rc;
+    pa::TreeArgs t;
+    t.block_table = block_table;
+    t.ctx_lens = ctx_lens;
+    t.tree_mask = tree_mask;
+    t.scratch = scratch_pages;
+    t.k_pool = k_pool;
+    t.v_pool = v_pool;
+    t.k_scale = k_scale;
+    t.v_scale = v_scale;
+    t.n_pages = n_pages;
+    t.n_seq = n_seq;
+    t.rows = width;
+    t.max_pages = max_pages_per_seq;
+    t.n_head_kv = n_head_kv;
+    t.head_dim = head_dim;
+    t.fp8 = kv_dtype == ATTN_KV_FP8_E4M3;
+    t.vtable = (int32_t*)workspace;
+    t.vlens = (int32_t*)((char*)workspace + off_lens);
+    // Each (sequence, row) is then a one-row decode over its branch view.
+    // (The split call's checks were done above or hold by construction.)
+    rc = from_hip(pa::launch_tree_stage(t, stream), fn);
+    if (rc != ATTN_OK)
+        return rc;
+    return split_call(fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, t.vtable,
+                      max_pages_per_seq, t.vlens, n_seq * width, n_head, n_head_kv, head_dim,
+                      page_size, kv_dtype, out, (char*)workspace + off_split,
+                      workspace_bytes - off_split, stream);
 }
 
 int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const void* v_pool,

@@ -109,4 +109,22 @@ struct CheckArgs {
 };
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 
+// Tree-shaped speculative round: per (sequence, row) branch views (tree.hip).
+struct TreeArgs {
+    const int32_t* block_table;
+    const int32_t* ctx_lens;
+    const int32_t* tree_mask;  // [n_seq][rows]: bit j = the row attends round row j
+    const int32_t* scratch;    // [n_seq][rows][2] pool pages reserved for the views
+    void* k_pool;
+    void* v_pool;
+    float* k_scale;
+    float* v_scale;
+    int64_t n_pages;
+    int32_t n_seq, rows, max_pages, n_head_kv, head_dim;
+    int fp8;
+    int32_t* vtable;  // out: [n_seq * rows][max_pages]
+    int32_t* vlens;   // out: [n_seq * rows]
+};
+hipError_t launch_tree_stage(const TreeArgs& a, hipStream_t stream);
+
 }  // namespace pa

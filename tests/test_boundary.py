@@ -114,6 +114,33 @@ def test_verify_width_rejects_unserved_group(pa):
     assert e.value.code == pa.ATTN_E_UNSUPPORTED
 
 
+def tree_args(**over):
+    a = decode_args(width=8, tree_mask=FAKE, scratch_pages=FAKE)
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(width=0), -2, "zero rows"), (dict(width=9), -3, "width 9"),
+    (dict(tree_mask=None), -1, "tree_mask"), (dict(scratch_pages=None), -1, "scratch_pages"),
+    (dict(n_seq=0), -2, "zero sequences"), (dict(n_seq=600), -3, "n_seq * width 4800"),
+    (dict(n_head=64, n_head_kv=2), -3, "query heads per kv head"),
+    (dict(workspace_bytes=1000), -4, "workspace has 1000 bytes"),
+    (dict(q=None), -1, "q is NULL"),
+])
+def test_verify_tree_host_checks(pa, over, code, needle):
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_verify_tree(**tree_args(**over))
+    assert e.value.code == code
+    assert needle in str(e.value)
+
+
+def test_tree_workspace_covers_eight_one_row_sequences_per_sequence(pa):
+    t = pa.attn_paged_workspace_bytes(4, 32, 257, 16, 256)
+    d = pa.attn_paged_workspace_bytes(0, 32 * 8, 257, 16, 256)
+    assert t >= d + 32 * 8 * (257 + 1) * 4
+
+
 @pytest.mark.parametrize("over,code,needle", [
     (dict(rows=0), -2, "zero rows"), (dict(rows=9), -3, "rows 9"),
     (dict(window=-1), -5, "window -1"), (dict(q=None), -1, "q is NULL"),
