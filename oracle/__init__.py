@@ -57,6 +57,8 @@ def _load():
         lib.oracle_paged_attention.argtypes = [
             P, i32, i32, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, P, P, i32]
         lib.oracle_paged_attention.restype = ctypes.c_int
+        lib.oracle_round_q_e4m3.argtypes = [P, i64, i32, P, P]
+        lib.oracle_round_q_e4m3.restype = ctypes.c_int
         lib.oracle_paged_attention_window.argtypes = [
             P, i32, i32, P, P, P, P, i64, P, i32, P, i32, i32, i32, i32, i32, i32, P, P, P, i32]
         lib.oracle_paged_attention_window.restype = ctypes.c_int
@@ -87,17 +89,21 @@ def default_threads() -> int:
 
 def paged_attention(q, k_pool, v_pool, block_table, ctx_lens, *, n_head, n_head_kv, head_dim,
                     page_size, kv_dtype=KV_BF16, k_scale=None, v_scale=None, row_mask=None,
-                    window=0, kv_floor=None, threads=None) -> np.ndarray:
+                    window=0, kv_floor=None, q_fp8=False, threads=None) -> np.ndarray:
     """fp64 attention of every row of ``q`` (uint16 bf16 bits, shape
     [n_seq, rows, n_head, head_dim]) over the paged pools.
 
     Row r of sequence s sits at position p = ctx_lens[s]-rows+r and attends
     to key positions max(kv_floor[s], p-window+1) .. p (window 0: no window;
     kv_floor None: floor 0).  ``row_mask`` ([n_seq, rows], nonzero =
-    compute) limits the work; skipped rows come back as NaN.
+    compute) limits the work; skipped rows come back as NaN.  ``q_fp8``:
+    every query vector is first rounded by ``round_q_e4m3`` (the fp8
+    prefill's QK^T), the rest is unchanged.
     """
     lib = _load()
     q = _c(q, np.uint16)
+    if q_fp8:
+        q = round_q_e4m3(q)
     assert q.ndim == 4 and q.shape[2] == n_head and q.shape[3] == head_dim
     n_seq, rows = q.shape[0], q.shape[1]
     bt = _c(block_table, np.int32)
@@ -144,6 +150,22 @@ def kv_append(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=
                               page_size, kv_dtype)
     if rc != 0:
         raise ValueError("oracle_kv_append failed with %d" % rc)
+
+
+def round_q_e4m3(q, return_exps=False):
+    """Query vectors rounded to E4M3 at a power-of-two scale per vector (the
+    last axis), returned as bf16 bits of the same shape; see
+    ``oracle_round_q_e4m3`` in attn_oracle.c for the rule."""
+    lib = _load()
+    qq = _c(q, np.uint16)
+    d = qq.shape[-1]
+    n = qq.size // d
+    out = np.empty_like(qq)
+    exps = np.empty(n, np.int32)
+    rc = lib.oracle_round_q_e4m3(_ptr(qq), n, d, _ptr(out), _ptr(exps))
+    if rc != 0:
+        raise ValueError("oracle_round_q_e4m3 failed with %d" % rc)
+    return (out, exps.reshape(qq.shape[:-1])) if return_exps else out
 
 
 def e4m3_value(codes) -> np.ndarray:

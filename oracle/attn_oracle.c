@@ -288,6 +288,68 @@ uint8_t oracle_e4m3_encode(float y)
 }
 
 /*
+ * oracle_round_q_e4m3 -- the query vectors of an fp8 prefill, rounded to
+ * E4M3 ("Radiance Architecture Plugins -- declaring a model", section
+ * "Declare: the metadata": the build context carries `attn_prefill_fp8` bits
+ * that the attention op takes as `prefill_fp8`).  The pages name the switch
+ * only; the reading here is the plainest one that keeps every step exact
+ * except the rounding itself:
+ *
+ *   per vector (one query row of one head, head_dim values):
+ *     amax = max_d |q_d|
+ *     e    = the smallest integer with amax <= 448 * 2^e, and at least -117
+ *            (so every rounded value below stays a normal number; an
+ *            all-zero vector takes -117)
+ *     q'_d = 2^e * value(nearest E4M3 code of q_d / 2^e, ties to even)
+ *
+ * q_d / 2^e lies in [-448, 448], so no code saturates; q'_d has at most 4
+ * significant bits and is exact in bf16.
+ *
+ *   q, out   bf16 bits [n_vec][head_dim]
+ *   exps     [n_vec] receives e (may be NULL)
+ * Returns 0, or -1 for a non-finite input element.
+ */
+int oracle_round_q_e4m3(const uint16_t *q, int64_t n_vec, int32_t head_dim, uint16_t *out,
+                        int32_t *exps)
+{
+    if (!q || !out || n_vec < 0 || head_dim <= 0)
+        return -1;
+    for (int64_t v = 0; v < n_vec; ++v) {
+        const uint16_t *x = q + v * head_dim;
+        double amax = 0.0;
+        for (int d = 0; d < head_dim; ++d) {
+            const double a = fabs(orc_bf16(x[d]));
+            if (!isfinite(a))
+                return -1;
+            if (a > amax)
+                amax = a;
+        }
+        int e = -117;
+        if (amax > 0.0) {
+            int ex;
+            const double m = frexp(amax, &ex); /* amax = m 2^ex, m in [0.5, 1) */
+            /* 448 = 0.875 * 2^9: amax <= 448 * 2^e  <=>  m 2^ex <= 0.875 2^(9+e) */
+            e = m <= 0.875 ? ex - 9 : ex - 8;
+            if (e < -117)
+                e = -117;
+        }
+        if (exps)
+            exps[v] = e;
+        for (int d = 0; d < head_dim; ++d) {
+            const double y = ldexp(orc_bf16(x[d]), -e); /* exact */
+            const uint8_t c = oracle_e4m3_encode((float)y);
+            orc_e4m3_init();
+            const float r = (float)ldexp(orc_e4m3_tab[c & 0x7F], e); /* exact */
+            uint32_t u;
+            memcpy(&u, &r, sizeof u);
+            u |= (uint32_t)(c & 0x80) << 24;
+            out[v * head_dim + d] = (uint16_t)(u >> 16);
+        }
+    }
+    return 0;
+}
+
+/*
  * oracle_kv_append -- write n_tok new K/V rows into their token slots.
  *
  *   k_new, v_new  bf16 bits [n_tok][n_head_kv][head_dim]
