@@ -218,9 +218,9 @@ class Bench:
             self.ev.destroy(b)
         return wall, sum(kern) / len(kern), sorted(kern)[len(kern) // 2]
 
-    def setup_prefill(self, name):
+    def setup_prefill(self, name, w=None):
         torch, pa, synth = self.torch, self.pa, self.synth
-        w = synth.WORKLOADS[name]
+        w = synth.WORKLOADS[name] if w is None else w
         inp = synth.draw(w, "cuda")
         k, v, ks, vs = synth.poison_pools(inp.n_pages, w, "cuda")
         kv = pa.KV_FP8_E4M3 if w.kv_fp8 else pa.KV_BF16
@@ -432,6 +432,51 @@ class Bench:
                 "split_kernel_median_us": round(kern[len(kern) // 2] * 1e3, 2),
                 "rows": S * width, "mean_branch_depth": round(depth / (S * width), 3)}
 
+    def time_prefill_fp8(self, steps=10, warmup=3, rounds=3):
+        """The 4,096-row chunk over 28,672 cached rows with an fp8 cache:
+        the plain prefill (bf16 QK^T of the decoded codes) against
+        ATTN_PREFILL_FP8_QK (QK^T on the fp8 matrix unit), kernel medians by
+        the library's kernel timer, best of interleaved rounds."""
+        torch, pa = self.torch, self.pa
+        w = self.synth.scaled(self.synth.WORKLOADS["prefill_4096_over_28672"], kv_fp8=True,
+                              name="prefill_4096_over_28672_fp8kv")
+        st = self.setup_prefill(None, w)
+        inp = st["inp"]
+        fl = prefill_flops(w.rows, st["C"], w)
+        best = {}
+        for _ in range(rounds):
+            for bits in (0, pa.ATTN_PREFILL_FP8_QK):
+                def call(timer=None):
+                    if timer is not None:
+                        pa.attn_set_kernel_timer(timer[0], timer[1])
+                    pa.attn_paged_prefill_fp8(st["q"], w.rows, st["k"], st["v"], st["ks"],
+                                              st["vs"], inp.n_pages, inp.table, w.max_pages,
+                                              st["C"], w.n_head, w.n_head_kv, w.head_dim, 16,
+                                              st["kv"], bits, st["out"])
+                for _ in range(warmup):
+                    call()
+                torch.cuda.synchronize()
+                evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
+                for i in range(steps):
+                    call(evs[i])
+                torch.cuda.synchronize()
+                kern = sorted(self.ev.elapsed_ms(a, b) for a, b in evs)
+                for a, b in evs:
+                    self.ev.destroy(a)
+                    self.ev.destroy(b)
+                med = kern[len(kern) // 2]
+                best[bits] = min(best.get(bits, med), med)
+        res = {}
+        for bits, tag in ((0, "bits0_bf16_qk"), (pa.ATTN_PREFILL_FP8_QK, "qk_fp8")):
+            ms = best[bits]
+            res[tag] = {"kernel_median_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                        "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+        res["flops_per_launch"] = fl
+        res["speedup"] = round(best[0] / best[pa.ATTN_PREFILL_FP8_QK], 3)
+        del st
+        torch.cuda.empty_cache()
+        return res
+
     def time_prefill(self, st, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
@@ -627,6 +672,13 @@ def main():
             sec["verify_32seq_widths_1_2_4_8"] = {"error": str(e)[:200]}
         torch.cuda.empty_cache()
         log("[bench] secondary done", sec["verify_32seq_widths_1_2_4_8"])
+        log("[bench] secondary fp8 prefill")
+        try:
+            sec["prefill_4096_over_28672_fp8kv_qk"] = b.time_prefill_fp8()
+        except Exception as e:  # report, keep the headline
+            sec["prefill_4096_over_28672_fp8kv_qk"] = {"error": str(e)[:200]}
+        torch.cuda.empty_cache()
+        log("[bench] secondary done", sec["prefill_4096_over_28672_fp8kv_qk"])
         log("[bench] secondary tree round")
         try:
             sec["verify_32seq_tree8"] = b.time_tree()

@@ -237,6 +237,36 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
                        attn_kv_dtype kv_dtype, void* out, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* prefill_fp8 bits of attn_paged_prefill_fp8. */
+#define ATTN_PREFILL_FP8_QK 1
+
+/*
+ * attn_paged_prefill_fp8 -- attn_paged_prefill with the fp8 switch the
+ * attention op carries ("Radiance Architecture Plugins -- declaring a
+ * model", section "Declare: the metadata": the build context's
+ * `attn_prefill_fp8` bits are passed as the op's `prefill_fp8`).  The pages
+ * do not define the bits; here:
+ *
+ *   0                    attn_paged_prefill, bit for bit.
+ *   ATTN_PREFILL_FP8_QK  (fp8 cache only) QK^T runs on the fp8 matrix unit:
+ *                        K with its stored E4M3 codes and page scale, and
+ *                        each query vector (one row, one head) rounded to
+ *                        E4M3 at the smallest power-of-two scale 2^e with
+ *                        max|q| <= 448 * 2^e (e >= -117), ties to even.
+ *                        Softmax and PV are as in attn_paged_prefill.
+ *
+ * Any other bit, or the QK bit with a bf16 cache, returns
+ * ATTN_E_UNSUPPORTED.  Layout, limits and errors otherwise as
+ * attn_paged_prefill; query elements must be finite.
+ */
+int attn_paged_prefill_fp8(const void* q, int32_t n_rows, const void* k_pool,
+                           const void* v_pool, const float* k_scale, const float* v_scale,
+                           int64_t n_pages, const int32_t* block_table,
+                           int32_t max_pages_per_seq, int32_t ctx_len, int32_t n_head,
+                           int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                           attn_kv_dtype kv_dtype, int32_t prefill_fp8, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * attn_paged_mixed -- a continuous-batching step: decode rows of
  * n_seq_decode sequences beside prefill chunks of the other sequences, in

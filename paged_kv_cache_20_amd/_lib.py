@@ -27,13 +27,14 @@ ATTN_OK = 0
 ATTN_E_ARG = -1
 ATTN_E_SHAPE = -2
 ATTN_E_UNSUPPORTED = -3
+ATTN_PREFILL_FP8_QK = 1
 ATTN_E_WORKSPACE = -4
 ATTN_E_RANGE = -5
 ATTN_E_DEVICE = -6
 
 EXPORTS = [
     "attn_paged_decode", "attn_paged_verify", "attn_paged_verify_width",
-    "attn_paged_verify_tree", "attn_paged_prefill",
+    "attn_paged_verify_tree", "attn_paged_prefill", "attn_paged_prefill_fp8",
     "attn_paged_mixed", "attn_paged_decode_window", "attn_paged_prefill_window",
     "attn_kv_append", "attn_block_table_build", "attn_paged_workspace_bytes", "attn_caps",
     "attn_check_lengths_host", "attn_check_block_table_host", "attn_check_device",
@@ -74,6 +75,9 @@ _lib.attn_paged_verify_tree.restype = ctypes.c_int
 _lib.attn_paged_prefill.argtypes = [_P, _I32, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32, _I32,
                                     _I32, _I32, _I32, _P, _P, _SZ, _P]
 _lib.attn_paged_prefill.restype = ctypes.c_int
+_lib.attn_paged_prefill_fp8.argtypes = [_P, _I32, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                        _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]
+_lib.attn_paged_prefill_fp8.restype = ctypes.c_int
 _lib.attn_paged_mixed.argtypes = [_P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _P, _I64, _P, _I32,
                                   _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]
 _lib.attn_paged_mixed.restype = ctypes.c_int
@@ -241,6 +245,16 @@ def attn_paged_prefill(q, n_rows, k_pool, v_pool, k_scale, v_scale, n_pages, blo
         _dp(q), n_rows, _dp(k_pool), _dp(v_pool), _dp(k_scale), _dp(v_scale), n_pages,
         _dp(block_table), max_pages_per_seq, ctx_len, n_head, n_head_kv, head_dim, page_size,
         kv_dtype, _dp(out), _dp(workspace), workspace_bytes, _stream(stream)))
+
+
+def attn_paged_prefill_fp8(q, n_rows, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                           max_pages_per_seq, ctx_len, n_head, n_head_kv, head_dim, page_size,
+                           kv_dtype, prefill_fp8, out, workspace=None, workspace_bytes=0,
+                           stream=None):
+    return _check(_lib.attn_paged_prefill_fp8(
+        _dp(q), n_rows, _dp(k_pool), _dp(v_pool), _dp(k_scale), _dp(v_scale), n_pages,
+        _dp(block_table), max_pages_per_seq, ctx_len, n_head, n_head_kv, head_dim, page_size,
+        kv_dtype, prefill_fp8, _dp(out), _dp(workspace), workspace_bytes, _stream(stream)))
 
 
 def attn_kv_append(k_new, v_new, slot_mapping, n_tok, k_pool, v_pool, k_scale, v_scale, n_pages,

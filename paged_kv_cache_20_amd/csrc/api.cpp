@@ -333,13 +333,19 @@ static int prefill_call(const char* fn, const void* q, int32_t n_rows, const voi
                         int64_t n_pages, const int32_t* block_table, int32_t max_pages_per_seq,
                         int32_t ctx_len, int32_t window, int32_t kv_floor, int32_t n_head,
                         int32_t n_head_kv, int32_t head_dim, int32_t page_size,
-                        attn_kv_dtype kv_dtype, void* out, hipStream_t stream)
+                        attn_kv_dtype kv_dtype, void* out, hipStream_t stream,
+                        int32_t prefill_fp8 = 0)
 {
     int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                           max_pages_per_seq, n_head, n_head_kv, head_dim, page_size, kv_dtype,
                           out);
     if (rc != ATTN_OK)
         return rc;
+    if (prefill_fp8 & ~ATTN_PREFILL_FP8_QK)
+        return fail(ATTN_E_UNSUPPORTED, "%s: prefill_fp8 bits 0x%x (only ATTN_PREFILL_FP8_QK)",
+                    fn, (unsigned)prefill_fp8);
+    if ((prefill_fp8 & ATTN_PREFILL_FP8_QK) && kv_dtype != ATTN_KV_FP8_E4M3)
+        return fail(ATTN_E_UNSUPPORTED, "%s: ATTN_PREFILL_FP8_QK needs an fp8 cache", fn);
     if (n_rows <= 0)
         return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (n_rows = %d)", fn, n_rows);
     if (ctx_len < n_rows)
@@ -378,6 +384,7 @@ static int prefill_call(const char* fn, const void* q, int32_t n_rows, const voi
     a.n_tok = n_rows;
     a.window = window;
     a.kv_floor = kv_floor;
+    a.qk_fp8 = (prefill_fp8 & ATTN_PREFILL_FP8_QK) != 0;
     return from_hip(pa::launch_prefill(a, stream), fn);
 }
 
@@ -457,6 +464,21 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
     return prefill_call("attn_paged_prefill", q, n_rows, k_pool, v_pool, k_scale, v_scale,
                         n_pages, block_table, max_pages_per_seq, ctx_len, 0, 0, n_head,
                         n_head_kv, head_dim, page_size, kv_dtype, out, stream);
+}
+
+int attn_paged_prefill_fp8(const void* q, int32_t n_rows, const void* k_pool,
+                           const void* v_pool, const float* k_scale, const float* v_scale,
+                           int64_t n_pages, const int32_t* block_table,
+                           int32_t max_pages_per_seq, int32_t ctx_len, int32_t n_head,
+                           int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                           attn_kv_dtype kv_dtype, int32_t prefill_fp8, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return prefill_call("attn_paged_prefill_fp8", q, n_rows, k_pool, v_pool, k_scale, v_scale,
+                        n_pages, block_table, max_pages_per_seq, ctx_len, 0, 0, n_head,
+                        n_head_kv, head_dim, page_size, kv_dtype, out, stream, prefill_fp8);
 }
 
 int attn_paged_prefill_window(const void* q, int32_t n_rows, const void* k_pool,

@@ -95,6 +95,9 @@ struct PrefillArgs {
     // means no window.  0 <= kv_floor <= the first row's position.
     int32_t window;
     int32_t kv_floor;
+    // fp8 cache only: QK^T on the fp8 matrix unit, K with its stored codes,
+    // each query vector rounded to E4M3 at a power-of-two scale.
+    int qk_fp8 = 0;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

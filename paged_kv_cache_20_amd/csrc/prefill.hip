@@ -55,6 +55,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS __attribute__((address_space(3)))
 
@@ -88,6 +89,18 @@ __device__ __forceinline__ int swz(int r)
 {
     return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) |
            ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+}
+
+// Physical 16-byte chunk of logical chunk c of an fp8 K row (CK chunks)
+// in LDS row r is c ^ swzk<CK>(r).  The QK^T operand reads take one chunk
+// of each of 16 consecutive rows: for 256-byte rows (a full bank line each)
+// swzk is one-to-one on r mod 16; for 128-byte rows (two to a bank line) it
+// is one-to-one on r / 2 mod 8, so the 8 rows sharing a half of the banks
+// hit different chunks.
+template <int CK>
+__device__ __forceinline__ int swzk(int r)
+{
+    return CK == 16 ? (r & 15) : ((r >> 1) & 7);
 }
 
 template <int D, bool FP8, int RT, int NW>
@@ -200,6 +213,22 @@ __device__ __forceinline__ void stage_load(Staged<G>& st, const uint8_t* pool, c
         st.s = 1.f;
 }
 
+// fp8 K kept as codes (QK^T on the fp8 matrix unit): rows of D bytes in
+// LDS, chunks swizzled by swzk.
+template <class G>
+__device__ __forceinline__ void stage_store_codes(const Staged<G>& st, char* buf, float* sc,
+                                                  int wave, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < G::SCH; ++i) {
+        const int c = i * 64 + lane;
+        const int key = wave * G::KPW + c / G::CPR, piece = c % G::CPR;
+        *(u32x4*)(buf + key * G::ROWB + (piece ^ swzk<G::CPR>(key)) * 16) = st.c[i];
+    }
+    if (lane == 0 && ((wave * G::KPW) & 15) == 0)
+        sc[(wave * G::KPW) >> 4] = st.s;
+}
+
 template <class G>
 __device__ __forceinline__ void stage_store(const Staged<G>& st, char* buf, float* sc, int wave,
                                             int lane)
@@ -243,10 +272,19 @@ __device__ __forceinline__ float row_sum4(float v)
     return v + __shfl_xor(v, 32, 64);
 }
 
-template <int D, bool FP8, int RT, int NW>
+// Two bf16 (a dword) to floats.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w)
+{
+    return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+template <int D, bool FP8, int RT, int NW, bool QF8>
 __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(PrefillArgs a)
 {
     using G = PGeo<D, FP8, RT, NW>;
+    static_assert(!QF8 || (FP8 && RT == 1), "fp8 QK^T: fp8 cache, one row tile per wave");
+    constexpr int QS = D / 128;  // k-steps of the fp8 QK^T (128 d-values each)
     constexpr bool STG = FP8;  // staged through registers (fp8) or LDS-direct (bf16)
     __shared__ __attribute__((aligned(1024))) char s_k0[G::TILEB];
     __shared__ __attribute__((aligned(1024))) char s_k1[G::TILEB];
@@ -312,6 +350,10 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
     // The lane's query row in each of the wave's row tiles (row n of 16).
     int row[RT], head[RT], pos[RT], klo[RT];
     u32x4 qop[RT][G::KSTEPS];  // Q^T operand: d = 32 st + 8 kb + 0..7
+    // fp8 Q^T operand: byte i of k-step st is d = 128 st + 32 kb + i, the
+    // query rounded to E4M3 at the power-of-two scale qsc of its vector.
+    i32x8 qf[RT][QS];
+    float qsc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int wrow = 16 * (RT * wave + rt) + n;  // row in the workgroup
@@ -323,9 +365,52 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         klo[rt] = key_floor(pos[rt]);
         const uint16_t* q =
             (const uint16_t*)a.q + ((tok0 + (valid ? row[rt] : 0)) * H + head[rt]) * D;
+        qsc[rt] = 1.f;
+        if constexpr (QF8) {
+            // The vector's largest magnitude (its d-values sit in the four
+            // lanes n + 16 kb), then the smallest 2^e with amax <= 448 2^e
+            // (448 = 0.875 2^9), e >= -117; then q / 2^e (exact) to E4M3,
+            // nearest, ties to even.
+            u32x4 raw[QS][4];
+            float amax = 0.f;
 #pragma unroll
-        for (int st = 0; st < G::KSTEPS; ++st)
-            qop[rt][st] = valid ? *(const u32x4*)(q + 32 * st + 8 * kb) : u32x4{0u, 0u, 0u, 0u};
+            for (int st = 0; st < QS; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    raw[st][j] = valid ? *(const u32x4*)(q + 128 * st + 32 * kb + 8 * j)
+                                       : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[st][j][w])),
+                                                 fabsf(bf16_hi(raw[st][j][w]))));
+                }
+            amax = row_max4(amax);
+            int e = -117;
+            if (amax > 0.f) {
+                int ex;
+                const float mt = frexpf(amax, &ex);
+                e = max(mt <= 0.875f ? ex - 9 : ex - 8, -117);
+            }
+            qsc[rt] = ldexpf(1.f, e);
+#pragma unroll
+            for (int st = 0; st < QS; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t w0 = raw[st][j][2 * h], w1 = raw[st][j][2 * h + 1];
+                        int c = __builtin_amdgcn_cvt_pk_fp8_f32(
+                            ldexpf(bf16_lo(w0), -e), ldexpf(bf16_hi(w0), -e), 0, false);
+                        c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(bf16_lo(w1), -e),
+                                                            ldexpf(bf16_hi(w1), -e), c, true);
+                        qf[rt][st][2 * j + h] = c;
+                    }
+        } else {
+#pragma unroll
+            for (int st = 0; st < G::KSTEPS; ++st)
+                qop[rt][st] =
+                    valid ? *(const u32x4*)(q + 32 * st + 8 * kb) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
 
     f32x4 O[RT][G::DBLK];
@@ -339,6 +424,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         l[rt] = 0.f;
     }
     const float sm_log2 = kLog2e / __builtin_sqrtf((float)D);
+    // Score factor of an fp8 page (times its K scale): with fp8 QK^T the
+    // query's power-of-two scale too (exact).
+    const float smq = QF8 ? sm_log2 * qsc[0] : sm_log2;
 
     if (tid == 0)
         s_bad = 0;
@@ -384,7 +472,30 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
     // S^T of a tile: [row tile][16-key block]; two sets, current and next.
     f32x4 sa[RT][4], sb[RT][4];
     float ka[4], kb4[4];  // K page scales (fp8) of the tile in sa / sb
+    const int skq = swzk<G::CPR>(n);  // fp8 K rows: 16 kq + n, swizzle of n
     auto scores = [&](const char* ks, f32x4 (&acc)[RT][4], int kq) {
+        if constexpr (QF8) {
+            // K codes of key row 16 kq + n: k-step st is logical chunks
+            // 8 st + 2 kb and + 1 (d = 128 st + 32 kb + 0..31).
+            const char* kr = ks + (16 * kq + n) * G::ROWB;
+            i32x8 kw8[QS];
+#pragma unroll
+            for (int st = 0; st < QS; ++st) {
+                const u32x4 c0 = *(const u32x4*)(kr + ((8 * st + 2 * kb) ^ skq) * 16);
+                const u32x4 c1 = *(const u32x4*)(kr + ((8 * st + 2 * kb + 1) ^ skq) * 16);
+                kw8[st] = i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
+                                (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                acc[rt][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < QS; ++st)
+                    acc[rt][kq] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        kw8[st], qf[rt][st], acc[rt][kq], 0, 0, 0, 0, 0, 0);
+            }
+            return;
+        }
         u32x4 kw[G::KSTEPS];
 #pragma unroll
         for (int st = 0; st < G::KSTEPS; ++st)
@@ -404,17 +515,23 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
     // whose first key is tile0 + wk.
     const int wk = ((wave * G::KPW) >> 4) * 16;
     Staged<G> stk, stv;
+    auto store_k = [&](char* buf, float* sc) {
+        if constexpr (QF8)
+            stage_store_codes<G>(stk, buf, sc, wave, lane);
+        else
+            stage_store<G>(stk, buf, sc, wave, lane);
+    };
     const int k0 = ts * kKT;
     int rawv = fetch_page(b, k0 + wk);        // block-table entries of the next V
     int rawk = fetch_page(b, k0 + kKT + wk);  // and K tiles to load
     if constexpr (STG) {
         stage_load<G>(stk, kp, a.k_scale, b, k0 + wk, wave, lane, rawv, &bad);
-        stage_store<G>(stk, s_k0, s_ksc[0], wave, lane);
+        store_k(s_k0, s_ksc[0]);
         stage_load<G>(stv, vp, a.v_scale, b, k0 + wk, wave, lane, rawv, &bad);
         stage_store<G>(stv, s_v0, s_vsc[0], wave, lane);
         if (nt > ts + 1) {
             stage_load<G>(stk, kp, a.k_scale, b, k0 + kKT + wk, wave, lane, rawk, &bad);
-            stage_store<G>(stk, s_k1, s_ksc[1], wave, lane);
+            store_k(s_k1, s_ksc[1]);
         }
     } else {
         issue_direct<G>(s_k0, kp, b, k0 + wk, wave, loff, rawv, &bad);
@@ -461,7 +578,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         float sx[4];  // factor applied to cur in the exponent
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq)
-            sx[kq] = FP8 ? kc[kq] * sm_log2 : sm_log2;
+            sx[kq] = FP8 ? kc[kq] * smq : sm_log2;
         float lmax[RT];
         if (diag) {
 #pragma unroll
@@ -582,7 +699,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
             if (t + 1 < nt)
                 stage_store<G>(stv, vwb, vws, wave, lane);
             if (t + 2 < nt)
-                stage_store<G>(stk, kwb, kws, wave, lane);
+                store_k(kwb, kws);
         } else {
             __builtin_amdgcn_s_waitcnt(0);
         }
@@ -617,7 +734,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
     }
 }
 
-template <int D, bool FP8, int RT, int NW>
+template <int D, bool FP8, int RT, int NW, bool QF8 = false>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream)
 {
     using G = PGeo<D, FP8, RT, NW>;
@@ -630,7 +747,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream)
     const int grid = (int)((nblk + 7) / 8) * 8;
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, stream);
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, RT, NW>), dim3(grid), dim3(G::NTH), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, RT, NW, QF8>), dim3(grid), dim3(G::NTH), 0, stream,
+                       a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_stop)
         (void)hipEventRecord(a.ev_stop, stream);
@@ -648,6 +766,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
     // wave's softmax overlaps the other's matrix work.  (Two row tiles per
     // wave halve the LDS reads per flop but need more than the 256 VGPRs of
     // a wave at this occupancy for head_dim 256.)
+    if (a.qk_fp8) {
+        if (!a.fp8)
+            return hipErrorNotSupported;
+        if (a.head_dim == 128)
+            return launch_t<128, true, 1, 8, true>(a, stream);
+        if (a.head_dim == 256)
+            return launch_t<256, true, 1, 8, true>(a, stream);
+        return hipErrorNotSupported;
+    }
     if (a.head_dim == 128)
         return a.fp8 ? launch_t<128, true, 1, 8>(a, stream) : launch_t<128, false, 1, 8>(a, stream);
     if (a.head_dim == 256)

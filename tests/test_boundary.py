@@ -287,3 +287,19 @@ def test_host_checkers(pa):
     with pytest.raises(pa.AttnError) as e:
         pa.attn_check_block_table_host(bt, [20, 20], 2, 16, 3)
     assert "block_table[1][1]" in str(e.value)
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(prefill_fp8=2), -3, "prefill_fp8 bits 0x2"),
+    (dict(prefill_fp8=1), -3, "needs an fp8 cache"),
+    (dict(prefill_fp8=1, kv_dtype=1, k_scale=FAKE, v_scale=FAKE, n_rows=0), -2, "zero rows"),
+    (dict(prefill_fp8=1, kv_dtype=1, k_scale=None, v_scale=None), -1, "fp8 kv needs"),
+    (dict(prefill_fp8=0, ctx_len=40000), -5, "exceeds"),
+])
+def test_prefill_fp8_host_checks(pa, over, code, needle):
+    args = prefill_args(prefill_fp8=0)
+    args.update(over)
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_prefill_fp8(**args)
+    assert e.value.code == code
+    assert needle in str(e.value)
