@@ -205,8 +205,12 @@ int attn_paged_verify_width(const void* q, const void* k_pool, const void* v_poo
  * attn_paged_verify_width rows.  Bytes are copied into the views, never
  * re-quantised, so with an fp8 pool a round must lie inside one page (one
  * scale); rows of a round that does not get NaN.  Needs n_seq * width <=
- * 4096 and at most 16 query heads per kv head.  Each row reads its whole
- * context (width times the bytes of a chain round).
+ * 4096 and at most 16 query heads per kv head.  The context below the
+ * 512-key split holding C0 is read once for all rows of a sequence (as by
+ * attn_paged_verify_width); that split and the next are read per row.
+ * Where attn_paged_verify_width would not serve `width` rows (its tile
+ * limit), every row reads its whole context instead; the results are the
+ * same bits.
  */
 int attn_paged_verify_tree(const void* q, void* k_pool, void* v_pool, float* k_scale,
                            float* v_scale, int64_t n_pages, const int32_t* block_table,

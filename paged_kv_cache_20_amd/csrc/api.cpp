@@ -127,19 +127,21 @@ size_t split_ws_bytes(int32_t rows, int32_t n_seq, int32_t max_pages, int32_t n_
     return (size_t)(o_bytes + rec * 2 * 4);
 }
 
-// Workspace of a tree round: the branch views' table rows and lengths, then
-// the split-K partials of n_seq * 8 one-row sequences.
+// Workspace of a tree round: the branch views' table rows, lengths and
+// floors, then the split-K partials of n_seq * 8 one-row sequences.
 size_t tree_ws_bytes(int32_t n_seq, int32_t max_pages, int32_t n_head, int32_t head_dim,
-                            size_t* off_lens, size_t* off_split)
+                     size_t* off_lens, size_t* off_floor, size_t* off_split)
 {
     const int64_t nv = (int64_t)n_seq * ATTN_VERIFY_ROWS;
     const size_t tb = (size_t)((nv * max_pages * 4 + 255) / 256 * 256);
     const size_t lb = (size_t)((nv * 4 + 255) / 256 * 256);
     if (off_lens)
         *off_lens = tb;
+    if (off_floor)
+        *off_floor = tb + lb;
     if (off_split)
-        *off_split = tb + lb;
-    return tb + lb + split_ws_bytes(1, (int32_t)nv, max_pages, n_head, head_dim);
+        *off_split = tb + 2 * lb;
+    return tb + 2 * lb + split_ws_bytes(1, (int32_t)nv, max_pages, n_head, head_dim);
 }
 
 
@@ -149,7 +151,7 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
                int32_t n_seq, int32_t n_head, int32_t n_head_kv, int32_t head_dim,
                int32_t page_size, attn_kv_dtype kv_dtype, void* out, void* workspace,
                size_t workspace_bytes, hipStream_t stream, int32_t window = 0,
-               const int32_t* kv_floor = nullptr)
+               const int32_t* kv_floor = nullptr, int below_round = 0, int phase = 0)
 {
     int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                           max_pages, n_head, n_head_kv, head_dim, page_size, kv_dtype, out);
@@ -173,6 +175,10 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     // addressed through a buffer resource spanning less than 2 GiB.
     if ((int64_t)rows * n_head * head_dim * 4 >= ((int64_t)1 << 31))
         return fail(ATTN_E_UNSUPPORTED, "%s: rows * n_head * head_dim too large", fn);
+    // A split's partials span its rows' records, max_split * n_head apart.
+    const int64_t ms = pa::max_splits(max_pages, ATTN_PAGE_SIZE);
+    if (((int64_t)(rows - 1) * ms * n_head + n_head) * head_dim * 4 >= ((int64_t)1 << 31))
+        return fail(ATTN_E_UNSUPPORTED, "%s: rows x splits x heads too large", fn);
     const size_t need = split_ws_bytes(rows, n_seq, max_pages, n_head, head_dim);
     rc = check_workspace(fn, workspace, workspace_bytes, need);
     if (rc != ATTN_OK)
@@ -206,6 +212,8 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     a.max_blocks = g_max_workgroups.load(std::memory_order_relaxed);
     a.window = window;
     a.kv_floor = kv_floor;
+    a.below_round = below_round;
+    a.phase = phase;
     return from_hip(pa::launch_split_decode(a, stream), fn);
 }
 
@@ -278,7 +286,9 @@ size_t attn_paged_workspace_bytes(int op, int32_t n_seq, int32_t max_pages_per_s
     case 1: return split_ws_bytes(ATTN_VERIFY_ROWS, n_seq, max_pages_per_seq, n_head, head_dim);
     case 2: return 0;
     case 3: return split_ws_bytes(1, n_seq, max_pages_per_seq, n_head, head_dim);
-    case 4: return tree_ws_bytes(n_seq, max_pages_per_seq, n_head, head_dim, nullptr, nullptr);
+    case 4:
+        return tree_ws_bytes(n_seq, max_pages_per_seq, n_head, head_dim, nullptr, nullptr,
+                             nullptr);
     default: return 0;
     }
 }
@@ -417,9 +427,9 @@ int attn_paged_verify_tree(const void* q, void* k_pool, void* v_pool, float* k_s
     if (n_head / n_head_kv > 16)
         return fail(ATTN_E_UNSUPPORTED, "%s: %d query heads per kv head (at most 16)", fn,
                     n_head / n_head_kv);
-    size_t off_lens = 0, off_split = 0;
-    const size_t need =
-        tree_ws_bytes(n_seq, max_pages_per_seq, n_head, head_dim, &off_lens, &off_split);
+    size_t off_lens = 0, off_floor = 0, off_split = 0;
+    const size_t need = tree_ws_bytes(n_seq, max_pages_per_seq, n_head, head_dim, &off_lens,
+                                      &off_floor, &off_split);
     rc = check_workspace(fn, workspace, workspace_bytes, need);
     if (rc != ATTN_OK)
         return rc;
@@ -441,15 +451,46 @@ int attn_paged_verify_tree(const void* q, void* k_pool, void* v_pool, float* k_s
     t.fp8 = kv_dtype == ATTN_KV_FP8_E4M3;
     t.vtable = (int32_t*)workspace;
     t.vlens = (int32_t*)((char*)workspace + off_lens);
-    // Each (sequence, row) is then a one-row decode over its branch view.
-    // (The split call's checks were done above or hold by construction.)
+    t.vfloor = (int32_t*)((char*)workspace + off_floor);
+    // Each (sequence, row) is a one-row decode over its branch view, in
+    // three launches that keep that arithmetic: (A) the splits wholly below
+    // the one holding C0 = ctx_len - width hold context only, the same keys
+    // for every row, so the round's split kernel computes them for all rows
+    // at once (a round row's arithmetic is the decode row's); (B) the split
+    // holding C0 and the next differ per branch: the one-row split kernel
+    // over the views, from the first key of C0's split; (C) the combine of
+    // each view over all its splits.  A and B write the same partial records
+    // ((sequence, row) = view, split, head).  The checks of the three calls
+    // were made above or hold by construction.
+    // Shapes the round's split kernel does not serve take the plain decode of
+    // every view over all its splits (one launch, the same bits).
+    void* ws = (char*)workspace + off_split;
+    const size_t wsb = workspace_bytes - off_split;
+    const int g = n_head / n_head_kv;
+    const int64_t ms = pa::max_splits(max_pages_per_seq, ATTN_PAGE_SIZE);
+    const bool shared =
+        pa::split_tiles(width, g) * head_dim <= 512 &&
+        ((int64_t)(width - 1) * ms * n_head + n_head) * head_dim * 4 < ((int64_t)1 << 31);
     rc = from_hip(pa::launch_tree_stage(t, stream), fn);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!shared)
+        return split_call(fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, t.vtable,
+                          max_pages_per_seq, t.vlens, n_seq * width, n_head, n_head_kv,
+                          head_dim, page_size, kv_dtype, out, ws, wsb, stream);
+    rc = split_call(fn, width, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                    max_pages_per_seq, ctx_lens, n_seq, n_head, n_head_kv, head_dim, page_size,
+                    kv_dtype, out, ws, wsb, stream, 0, nullptr, 1, 1);
+    if (rc != ATTN_OK)
+        return rc;
+    rc = split_call(fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, t.vtable,
+                    max_pages_per_seq, t.vlens, n_seq * width, n_head, n_head_kv, head_dim,
+                    page_size, kv_dtype, out, ws, wsb, stream, 0, t.vfloor, 0, 1);
     if (rc != ATTN_OK)
         return rc;
     return split_call(fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, t.vtable,
                       max_pages_per_seq, t.vlens, n_seq * width, n_head, n_head_kv, head_dim,
-                      page_size, kv_dtype, out, (char*)workspace + off_split,
-                      workspace_bytes - off_split, stream);
+                      page_size, kv_dtype, out, ws, wsb, stream, 0, nullptr, 0, 2);
 }
 
 int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const void* v_pool,

@@ -485,10 +485,13 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             return key_floor(C - R, a.window, f);
         };
         auto nfull = [&](int C, int lo) {
-            return ctx_ok(C, R, cap) && lo >= 0 ? (C / kChunk - lo / kChunk) * Hk : 0;
+            if (!ctx_ok(C, R, cap) || lo < 0)
+                return 0;
+            const int end = a.below_round ? (C - R) / kChunk : C / kChunk;
+            return max(end - lo / kChunk, 0) * Hk;
         };
         auto npart = [&](int C, int lo) {
-            return ctx_ok(C, R, cap) && lo >= 0 && C % kChunk != 0 ? Hk : 0;
+            return ctx_ok(C, R, cap) && lo >= 0 && !a.below_round && C % kChunk != 0 ? Hk : 0;
         };
         const int per = (S + 255) / 256;
         const int b0 = tid * per;
@@ -704,9 +707,11 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         // stores: an empty slot stores at kFar, which the resource drops, so
         // no store sits under a branch either.
         const float qnan = __builtin_nanf("");
-        const int64_t rec0 = ((int64_t)s * a.max_split + j) * R * H;  // record (s, j, row 0, head 0)
-        const __amdgpu_buffer_rsrc_t ro = rsrc(a.o_part + rec0 * D, (uint32_t)(R * H * D * 4));
-        const __amdgpu_buffer_rsrc_t rml = rsrc(a.ml_part + rec0 * 2, (uint32_t)(R * H * 2 * 4));
+        const int64_t rs = (int64_t)a.max_split * H;  // records per row
+        const int64_t rec0 = (int64_t)s * R * rs + (int64_t)j * H;  // record (s, row 0, j, head 0)
+        const int64_t nrec = (R - 1) * rs + H;  // through record (s, R - 1, j, H - 1)
+        const __amdgpu_buffer_rsrc_t ro = rsrc(a.o_part + rec0 * D, (uint32_t)(nrec * D * 4));
+        const __amdgpu_buffer_rsrc_t rml = rsrc(a.ml_part + rec0 * 2, (uint32_t)(nrec * 2 * 4));
 #pragma unroll
         for (int tau = 0; tau < NT; ++tau) {
 #pragma unroll
@@ -715,7 +720,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
                 const int row = slot_row(slot, cur.tau0 + tau, g, ppt, R, cmr_mod);
                 const int h = kh * g + (slot % g);
                 const uint32_t off =
-                    row >= 0 ? (uint32_t)(((row * H + h) * D + n * G::DB) * 4) : kFar;
+                    row >= 0 ? (uint32_t)(((row * rs + h) * D + n * G::DB) * 4) : kFar;
 #pragma unroll
                 for (int jb = 0; jb < G::DB; jb += 4) {
                     const f32x4 v = bad ? f32x4{qnan, qnan, qnan, qnan}
@@ -727,7 +732,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             }
             const int row = slot_row(n, cur.tau0 + tau, g, ppt, R, cmr_mod);
             const int h = kh * g + (n % g);
-            const uint32_t off = (kb == 0 && row >= 0) ? (uint32_t)((row * H + h) * 8) : kFar;
+            const uint32_t off = (kb == 0 && row >= 0) ? (uint32_t)((row * rs + h) * 8) : kFar;
             const f32x2 v = bad ? f32x2{qnan, qnan} : f32x2{m[tau], l[tau]};
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rml, off, 0, 0);
         }
@@ -786,9 +791,10 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
     const int pos = C - R + r;
     const int ns = pos / kChunk + 1;
     const int jlo = key_floor(pos, a.window, f_s) / kChunk;  // first split the row attends
-    const float* ml = a.ml_part + (((int64_t)s * a.max_split * R + r) * H + h) * 2;
-    const float* op = a.o_part + (((int64_t)s * a.max_split * R + r) * H + h) * D + lane * E;
-    const int64_t mls = (int64_t)R * H * 2, ops = (int64_t)R * H * D;  // per-split strides
+    const int64_t rec = ((int64_t)s * R + r) * a.max_split * H + h;  // record (s, r, 0, h)
+    const float* ml = a.ml_part + rec * 2;
+    const float* op = a.o_part + rec * D + lane * E;
+    const int64_t mls = (int64_t)H * 2, ops = (int64_t)H * D;  // per-split strides
 
     // Splits in groups of 64, lane = split within the group.
     float M = neg_inf();
@@ -881,15 +887,19 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
         blocks = a.max_blocks;
     if (blocks < 1)
         blocks = 1;
-    if (a.ev_start)
-        (void)hipEventRecord(a.ev_start, stream);
-    hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    if (a.ev_stop)
-        (void)hipEventRecord(a.ev_stop, stream);
+    if (a.phase != 2) {
+        if (a.ev_start)
+            (void)hipEventRecord(a.ev_start, stream);
+        hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        if (a.ev_stop)
+            (void)hipEventRecord(a.ev_stop, stream);
+    }
+    if (a.phase == 1)
+        return hipSuccess;
     const int64_t waves = (int64_t)a.n_seq * a.rows * a.n_head;
     hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)((waves + kWaves - 1) / kWaves)),
                        dim3(256), 0, stream, a);

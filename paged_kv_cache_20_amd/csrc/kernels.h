@@ -33,8 +33,10 @@ struct SplitArgs {
     int32_t n_seq, n_head, n_head_kv, head_dim, rows;
     int fp8;
     void* out;
-    float* o_part;   // [n_seq][max_split][rows][n_head][head_dim]
-    float* ml_part;  // [n_seq][max_split][rows][n_head][2]
+    // Split partials, row-major per (sequence, row): the records of a call
+    // with (n_seq, rows) and of one with (n_seq * rows, 1) coincide.
+    float* o_part;   // [n_seq][rows][max_split][n_head][head_dim]
+    float* ml_part;  // [n_seq][rows][max_split][n_head][2]
     int32_t max_split;
     hipEvent_t ev_start, ev_stop;  // optional timing pair around the split kernel
     int32_t max_blocks;            // grid bound for the split kernel; 0 = fill the device
@@ -44,6 +46,11 @@ struct SplitArgs {
     int32_t window;
     const int32_t* kv_floor;
     int32_t slices;  // work items per (sequence, split, kv head); set by the launcher
+    // Only the full splits below the one holding the call's first row
+    // (0 .. (C - rows) / 512 - 1): the context shared by every row of a round.
+    int below_round = 0;
+    // 0: split kernel then combine; 1: split kernel only; 2: combine only.
+    int phase = 0;
 };
 
 // Decode (rows = 1) and verify (rows = 8): split kernel + fixed-order combine.
@@ -127,6 +134,7 @@ struct TreeArgs {
     int fp8;
     int32_t* vtable;  // out: [n_seq * rows][max_pages]
     int32_t* vlens;   // out: [n_seq * rows]
+    int32_t* vfloor;  // out: [n_seq * rows], first key of the split holding C - rows
 };
 hipError_t launch_tree_stage(const TreeArgs& a, hipStream_t stream);
 

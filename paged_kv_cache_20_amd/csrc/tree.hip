@@ -84,8 +84,10 @@ __global__ __launch_bounds__(256) void tree_stage_kernel(TreeArgs a)
         }
         vt[e] = v;
     }
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         a.vlens[sr] = ok ? L : 0;
+        a.vfloor[sr] = ok ? (C0 / kChunk) * kChunk : 0;
+    }
     if (!ok)
         return;
 

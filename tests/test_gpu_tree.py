@@ -118,8 +118,13 @@ def oracle_branch(oc, inp, s, r, pos):
 
 
 CASES = [
-    tree_workload("tr_bf16_d128_g4", [8, 300, 531, 1300], 8, 8, 2, 128, False, 111),
-    tree_workload("tr_bf16_d256_g4_w5", [12, 700, 1029], 5, 16, 4, 256, False, 112),
+    # 1029 - 8 and 2051 - 8 put a round across a 512-key split boundary
+    tree_workload("tr_bf16_d128_g4", [8, 300, 531, 1029, 1300, 2051], 8, 8, 2, 128, False, 111),
+    tree_workload("tr_bf16_d256_g4_w5", [12, 700, 1029, 1538], 5, 16, 4, 256, False, 112),
+    # 16 heads per kv head: the round's split kernel does not serve 3 rows at
+    # head_dim 256 (or 8 at 128), so every view is decoded alone
+    tree_workload("tr_bf16_d256_g16_w3", [5, 514, 900], 3, 32, 2, 256, False, 115),
+    tree_workload("tr_bf16_d128_g16_w8", [9, 515, 1030], 8, 32, 2, 128, False, 116),
     # fp8: every round inside one page (C0 % 16 + R <= 16: 0, 3, 0, 0)
     tree_workload("tr_fp8_d128_g4", [8, 523, 1000, 4104], 8, 32, 8, 128, True, 113),
 ]
@@ -162,9 +167,17 @@ def test_chain_tree_is_the_width_round(case):
     wsb = pa.attn_paged_workspace_bytes(1, S, inp.table.shape[1], w.n_head, w.head_dim)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     ref = torch.empty_like(inp.q)
-    pa.attn_paged_verify_width(inp.q, gpu.k, gpu.v, gpu.ks, gpu.vs, inp.n_pages, inp.table,
-                               inp.table.shape[1], inp.lengths, S, R, w.n_head, w.n_head_kv,
-                               w.head_dim, PAGE, gpu.kv, ref, ws, wsb)
+    try:
+        pa.attn_paged_verify_width(inp.q, gpu.k, gpu.v, gpu.ks, gpu.vs, inp.n_pages, inp.table,
+                                   inp.table.shape[1], inp.lengths, S, R, w.n_head, w.n_head_kv,
+                                   w.head_dim, PAGE, gpu.kv, ref, ws, wsb)
+    except pa.AttnError as e:
+        # a width the round kernel does not serve: the chain rows are the
+        # decode rows at their positions
+        assert e.code == pa.ATTN_E_UNSUPPORTED
+        for r in range(R):
+            lens = inp.lengths - R + r + 1
+            ref[:, r:r + 1] = gpu.run("decode", q=inp.q[:, r:r + 1].contiguous(), lengths=lens)
     torch.cuda.synchronize()
     assert same_bits(out, ref)
 
@@ -175,12 +188,12 @@ def test_bad_mask_gives_nan_row_only(case):
     masks = random_masks(S, R, 9)
     good = run_tree(gpu, inp, masks, scratch_for(inp))
     bad = masks.copy()
-    bad[1, 2] |= 1 << (R - 1)   # names a later row
-    bad[2, 3] &= ~(1 << 3)      # does not name itself
+    bad[1, 0] |= 1 << (R - 1)        # names a later row
+    bad[2, R - 1] &= ~(1 << (R - 1))  # does not name itself
     out = run_tree(gpu, inp, bad, scratch_for(inp))
-    assert torch.isnan(out[1, 2].float()).all() and torch.isnan(out[2, 3].float()).all()
+    assert torch.isnan(out[1, 0].float()).all() and torch.isnan(out[2, R - 1].float()).all()
     keep = torch.ones(S, R, dtype=torch.bool)
-    keep[1, 2] = keep[2, 3] = False
+    keep[1, 0] = keep[2, R - 1] = False
     assert same_bits(out[keep.cuda()], good[keep.cuda()])
 
 
