@@ -15,9 +15,12 @@ HBM).  `roofline` times the split-K attention kernel alone with HIP events
 (recorded by the library on the call's stream) and prices its algorithmic
 bytes against 8 TB/s.  `secondary` times the other workloads the same way:
 single-sequence decode (latency), 64-sequence bf16 decode at head_dim 256,
-the 8-row verify round, and the 4096-row prefill chunk (bf16 MFMA TFLOP/s).
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the headline
-workload on this host.
+the 8-row verify round, the 4096-row prefill chunk (bf16 MFMA TFLOP/s), and
+the extended calls on the same shapes: a 4096-key sliding window, rounds of
+widths 1/2/4/8, the fp8-cache chunk with QK^T on the fp8 unit, 8-row tree
+rounds and the mixed decode + chunk step.  `cpu_baseline` is the CPU oracle
+timed over the whole headline workload on this host (repeated to about 10 s,
+median pass).
 
 `roofline.traffic` is the measured HBM bytes per launch of the timed kernel,
 read from profiles/hbm_traffic.json when that file was taken on the current
@@ -135,26 +138,6 @@ def traffic_from_profiles(kernel_key):
     return e.get("bytes_per_launch")
 
 
-def mixed_inputs(torch, synth, seed=1006):
-    """A continuous-batching step: 256 decode sequences of the fp8 decode
-    workload's shape (H 32 / Hk 8, d 128, fp8 e4m3, lengths log-uniform in
-    [2048, 32768], drawn with `seed` on the CPU) followed by one 2048-row
-    prefill chunk after 6144 cached rows of the same layer."""
-    gen = torch.Generator(device="cpu")
-    gen.manual_seed(seed)
-    dec = synth.scaled(synth.WORKLOADS["decode_256seq_fp8"], seed=seed)
-    lens = synth.draw_lengths(dec, gen).tolist() + [8192]
-    w = synth.listed("mixed_256dec_fp8_plus_2048chunk", lens, 1, 32, 8, 128, True, seed)
-    inp = synth.draw(w, "cuda")
-    q_rows = [1] * 256 + [2048]
-    gq = torch.Generator(device="cuda")
-    gq.manual_seed(seed + 1)
-    q = synth.normal_bf16((sum(q_rows), 32, 128), gq)
-    cu = torch.tensor([0] + list(__import__("itertools").accumulate(q_rows)), dtype=torch.int32,
-                      device="cuda")
-    return w, inp, q, cu, lens
-
-
 class Bench:
     def __init__(self, torch, pa, synth):
         self.torch, self.pa, self.synth = torch, pa, synth
@@ -252,7 +235,7 @@ class Bench:
         half (attn_paged_decode) and its chunk half (attn_paged_prefill)
         called alone."""
         torch, pa, synth = self.torch, self.pa, self.synth
-        w, inp, q, cu, lens = mixed_inputs(torch, synth)
+        w, inp, q, cu, lens = synth.mixed_step()
         k, v, ks, vs = synth.poison_pools(inp.n_pages, w, "cuda")
         kv = pa.KV_FP8_E4M3
         pa.attn_kv_append(inp.k_src, inp.v_src, inp.slots, inp.slots.numel(), k, v, ks, vs,
@@ -390,12 +373,7 @@ class Bench:
         st = self.setup_split("verify_32seq_8rows", spare_pages=2 * 32 * width)
         w, inp = st["w"], st["inp"]
         S = w.n_seq
-        rng = np.random.default_rng(1008)
-        masks = np.zeros((S, width), np.int32)
-        for s in range(S):
-            for r in range(width):
-                par = int(rng.integers(-1, r))
-                masks[s, r] = (1 << r) | (masks[s, par] if par >= 0 else 0)
+        masks = self.synth.tree_masks(S, width, 1008)
         used = set(inp.table.cpu().numpy().ravel().tolist())
         free = [p for p in range(inp.n_pages) if p not in used][:2 * S * width]
         scratch = torch.tensor(free, dtype=torch.int32, device="cuda")

@@ -188,3 +188,38 @@ def bits(t: torch.Tensor):
     if t.dtype == torch.uint8:
         return t.numpy()
     return t.numpy()
+
+
+def mixed_step(seed: int = 1006):
+    """A continuous-batching step: 256 decode sequences of the fp8 decode
+    workload's shape (H 32 / Hk 8, d 128, fp8 e4m3, lengths log-uniform in
+    [2048, 32768], drawn with `seed` on the CPU) followed by one 2048-row
+    prefill chunk after 6144 cached rows of the same layer.
+    Returns (workload, inputs, q [256 + 2048][32][128], cu_seqlens, lengths)."""
+    import itertools
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    dec = scaled(WORKLOADS["decode_256seq_fp8"], seed=seed)
+    lens = draw_lengths(dec, gen).tolist() + [8192]
+    w = listed("mixed_256dec_fp8_plus_2048chunk", lens, 1, 32, 8, 128, True, seed)
+    inp = draw(w, "cuda")
+    q_rows = [1] * 256 + [2048]
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(seed + 1)
+    q = normal_bf16((sum(q_rows), 32, 128), gq)
+    cu = torch.tensor([0] + list(itertools.accumulate(q_rows)), dtype=torch.int32, device="cuda")
+    return w, inp, q, cu, lens
+
+
+def tree_masks(n_seq: int, rows: int, seed: int):
+    """Random speculative trees: row r's parent is drawn uniformly among the
+    earlier rows and "none" (numpy PCG64 with `seed`); its mask names r and
+    its parent's mask.  int32 [n_seq][rows]."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    masks = np.zeros((n_seq, rows), np.int32)
+    for s in range(n_seq):
+        for r in range(rows):
+            par = int(rng.integers(-1, r))
+            masks[s, r] = (1 << r) | (masks[s, par] if par >= 0 else 0)
+    return masks
