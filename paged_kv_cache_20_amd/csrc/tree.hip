@@ -13,10 +13,12 @@
 // This file builds, for every (sequence, row), that branch view: a private
 // copy of the page holding C0 (its context rows and the branch tokens that
 // land in it) and of the next page if the branch spills into it, written to
-// two caller-reserved pool pages, and a block-table row that is the
-// sequence's own up to the page before C0 and the private pages after.  The
-// decode kernel then runs once per (sequence, row) over these views, so a
-// row's arithmetic is exactly the decode's.  Bytes are copied, never
+// two caller-reserved pool pages, a block-table row that is the sequence's
+// own up to the page before C0 and the private pages after, the view's length
+// and the first key of the 512-key split holding C0.  The decode kernels then
+// run over the views (the splits below C0's on the sequence's own pages for
+// all rows at once, C0's split and the next per view, then one combine per
+// view), so a row's arithmetic is exactly the decode's.  Bytes are copied, never
 // re-quantised: an fp8 view needs every copied token to share its page's
 // scale, which holds when the round lies inside one page; a row whose view
 // cannot be formed (bad mask, bad page, fp8 round across a page boundary)
