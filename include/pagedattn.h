@@ -206,7 +206,8 @@ int attn_paged_verify_width(const void* q, const void* k_pool, const void* v_poo
  * re-quantised, so with an fp8 pool a round must lie inside one page (one
  * scale); rows of a round that does not get NaN.  Needs n_seq * width <=
  * 4096 and at most 16 query heads per kv head.  The context below the
- * 512-key split holding C0 is read once for all rows of a sequence (as by
+ * split holding C0 (splits of 1024 keys with an fp8 cache at head_dim 128,
+ * else 512) is read once for all rows of a sequence (as by
  * attn_paged_verify_width); that split and the next are read per row.
  * Where attn_paged_verify_width would not serve `width` rows (its tile
  * limit), every row reads its whole context instead; the results are the

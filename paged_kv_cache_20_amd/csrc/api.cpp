@@ -452,6 +452,7 @@ int attn_paged_verify_tree(const void* q, void* k_pool, void* v_pool, float* k_s
     t.vtable = (int32_t*)workspace;
     t.vlens = (int32_t*)((char*)workspace + off_lens);
     t.vfloor = (int32_t*)((char*)workspace + off_floor);
+    t.chunk = pa::decode_chunk(head_dim, kv_dtype == ATTN_KV_FP8_E4M3);
     // Each (sequence, row) is a one-row decode over its branch view, in
     // three launches that keep that arithmetic: (A) the splits wholly below
     // the one holding C0 = ctx_len - width hold context only, the same keys

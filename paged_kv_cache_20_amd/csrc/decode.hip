@@ -6,8 +6,9 @@
 // at position ctx_len - R + r ($defs.Fill "seq_len" counts the call's rows).
 //
 // Work decomposition
-//   A work item is (sequence s, split j, kv head kh): keys [512 j, 512 j + 512)
-//   of s, clipped to ctx_len.  Split boundaries are absolute multiples of 512,
+//   A work item is (sequence s, split j, kv head kh): keys [P j, P j + P) of
+//   s, clipped to ctx_len, with P = 1024 for the fp8 cache at head_dim 128
+//   and 512 otherwise.  Split boundaries are absolute multiples of P,
 //   so the items a row takes part in, and everything computed inside them,
 //   depend on the row's position and its sequence's own data only.  Each wave
 //   of a persistent grid walks items (wave, wave + total waves, ...); which
@@ -45,7 +46,7 @@
 //   P, both per page.  Keys past a row's position are masked; a fully masked
 //   tile leaves m, l and O bit-identical.
 //
-// Combine: per (sequence, row, head), splits 0 .. floor(pos / 512) are merged
+// Combine: per (sequence, row, head), splits 0 .. floor(pos / P) are merged
 // in a fixed order that depends on their count only: M = max m_j,
 // w_j = exp2(m_j - M), den = sum w_j l_j (a fixed butterfly inside each group
 // of 64 splits, groups in increasing order), num = sum w_j o_j (j
@@ -124,6 +125,8 @@ struct Geo {
     // keeps a tile at 16 KiB.  A property of (head_dim, dtype) only, so a
     // row's arithmetic never depends on how many rows the call has.
     static constexpr int KT = (!FP8 && D == 256) ? 16 : 32;
+    // Keys per split (see decode_chunk); likewise fixed per (head_dim, dtype).
+    static constexpr int CHUNK = (D == 128 && FP8) ? 1024 : 512;
     static constexpr int KB = KT / 16;          // 16-key blocks per tile
     static constexpr int KEYS = 4 * KB;         // keys a lane feeds to the PV product
 };
@@ -149,7 +152,7 @@ struct Plan {
     static constexpr int RAW = G::KB * G::KLD * 4 + G::KEYS * G::VDW;  // dwords per tile
     static constexpr int QOP = NT * G::STEPS * 4;
     static constexpr int OREG = NT * G::DB * 4;
-    static constexpr int ITEM_TILES = kChunk / G::KT;
+    static constexpr int ITEM_TILES = G::CHUNK / G::KT;
     static constexpr int OCC = (2 * RAW + QOP + OREG <= 176) ? 2 : 1;
     static constexpr int NBUF =
         OCC == 2 ? ((4 * RAW + 2 * QOP + OREG <= 192) ? 4 : 2)
@@ -405,7 +408,7 @@ __device__ __forceinline__ int key_floor(int pos, int window, int floor_s)
 // partial last splits (sequence, kv head): a wave's later items are the
 // short ones, so the grid's last round is short.  s_pre / s_pp: exclusive
 // prefixes over sequences of their full / partial items.
-template <int KT, int NT>
+template <int KT, int NT, int CH>
 __device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, const int* s_len,
                                              const int* s_lo, int S, int Hk, int slices,
                                              int item_in)
@@ -431,15 +434,15 @@ __device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, 
     const int local = __builtin_amdgcn_readfirstlane(key - pre[it.s]);
     it.C = __builtin_amdgcn_readfirstlane(s_len[it.s]);
     const int lo_s = __builtin_amdgcn_readfirstlane(s_lo[it.s]);
-    const int j0 = lo_s / kChunk;  // the sequence's first split with keys to attend
-    it.j = full ? j0 + local / Hk : it.C / kChunk;
+    const int j0 = lo_s / CH;  // the sequence's first split with keys to attend
+    it.j = full ? j0 + local / Hk : it.C / CH;
     it.kh = full ? local - (local / Hk) * Hk : local;
     // Tiles keep their absolute grid (a multiple of KT from the split start)
     // whatever the window, so a row's arithmetic does not depend on it.
-    const int base = it.j * kChunk;
+    const int base = it.j * CH;
     it.lo = max(lo_s, base);
     it.t0 = base + ((it.lo - base) / KT) * KT;
-    it.t1 = min(base + kChunk, it.C);
+    it.t1 = min(base + CH, it.C);
     it.npg = (it.t1 - it.t0 + 15) >> 4;
     it.tau0 = __builtin_amdgcn_readfirstlane(tau0);
     return it;
@@ -487,11 +490,12 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         auto nfull = [&](int C, int lo) {
             if (!ctx_ok(C, R, cap) || lo < 0)
                 return 0;
-            const int end = a.below_round ? (C - R) / kChunk : C / kChunk;
-            return max(end - lo / kChunk, 0) * Hk;
+            const int end = a.below_round ? (C - R) / G::CHUNK : C / G::CHUNK;
+            return max(end - lo / G::CHUNK, 0) * Hk;
         };
         auto npart = [&](int C, int lo) {
-            return ctx_ok(C, R, cap) && lo >= 0 && !a.below_round && C % kChunk != 0 ? Hk : 0;
+            return ctx_ok(C, R, cap) && lo >= 0 && !a.below_round && C % G::CHUNK != 0 ? Hk
+                                                                                       : 0;
         };
         const int per = (S + 255) / 256;
         const int b0 = tid * per;
@@ -615,10 +619,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     // are not computed), so every item starts at ring slot 0.
     // Table entries are fetched two items ahead and held in registers one
     // item ahead, so the ring never waits for them.
-    Item cur = resolve_item<KT, NT>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, item);
+    Item cur = resolve_item<KT, NT, G::CHUNK>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, item);
     int pid = fetch_pages(a, cur, true);
     bool has_next = item + nwaves < total;
-    Item nxt = resolve_item<KT, NT>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next ? item + nwaves : item);
+    Item nxt = resolve_item<KT, NT, G::CHUNK>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next ? item + nwaves : item);
     int pid_n = fetch_pages(a, nxt, has_next);
     // A full wait (never too weak): the loop then finds pid and pid_n
     // resolved on entry as it does on every later iteration, and its
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         // The item after next: geometry and table entries now.
         const int next2 = item + 2 * nwaves;
         const bool has_next2 = next2 < total;
-        const Item nxt2 = resolve_item<KT, NT>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next2 ? next2 : item);
+        const Item nxt2 = resolve_item<KT, NT, G::CHUNK>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next2 ? next2 : item);
         const int pid_nn = fetch_pages(a, nxt2, has_next2);
 
         const int s = cur.s, j = cur.j, kh = cur.kh, C = cur.C, t0 = cur.t0, t1 = cur.t1;
@@ -789,8 +793,8 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
         return;
     }
     const int pos = C - R + r;
-    const int ns = pos / kChunk + 1;
-    const int jlo = key_floor(pos, a.window, f_s) / kChunk;  // first split the row attends
+    const int ns = (pos >> a.chunk_log2) + 1;
+    const int jlo = key_floor(pos, a.window, f_s) >> a.chunk_log2;  // first split the row attends
     const int64_t rec = ((int64_t)s * R + r) * a.max_split * H + h;  // record (s, r, 0, h)
     const float* ml = a.ml_part + rec * 2;
     const float* op = a.o_part + rec * D + lane * E;
@@ -859,8 +863,12 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
 }
 
 template <int D, bool FP8, int NT, bool WIN>
-hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
+hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
 {
+    using G = Geo<D, FP8>;
+    static_assert((G::CHUNK & (G::CHUNK - 1)) == 0, "split size: a power of two");
+    SplitArgs a = a0;
+    a.chunk_log2 = __builtin_ctz((unsigned)G::CHUNK);
     static int s_grid[64] = {0};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -876,6 +884,10 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream)
                                                          0);
         if (e != hipSuccess)
             return e;
+        // 1024-key splits: one workgroup per CU keeps about as many items per
+        // wave as 512-key splits at two (the load stream is as fast).
+        if (G::CHUNK > kChunk && per > 1)
+            per = 1;
         grid_cap = cus * (per > 0 ? per : 1);
     }
     const int Hk = a.n_head_kv;

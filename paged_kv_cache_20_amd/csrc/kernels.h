@@ -7,10 +7,14 @@
 
 namespace pa {
 
-// Tokens per split of the split-K decode/verify kernel.  Split boundaries sit
-// at absolute multiples of this value, so a row's partial results depend only
-// on its own position and context -- never on batch size or row count.
+// Tokens per split of the split-K decode/verify kernel: a property of the
+// (head_dim, KV dtype) instantiation, 1024 for the fp8 cache at head_dim 128
+// (half the split partials to store and combine) and 512 otherwise.  Split
+// boundaries sit at absolute multiples of it, so a row's partial results
+// depend only on its own position and context -- never on batch size or row
+// count.  kChunk, the smallest, sizes workspaces.
 constexpr int kChunk = 512;
+inline int decode_chunk(int32_t head_dim, bool fp8) { return head_dim == 128 && fp8 ? 1024 : 512; }
 // Largest batch the decode/verify kernels take (the per-block prefix over
 // sequences lives in LDS).
 constexpr int kMaxSeq = 4096;
@@ -51,6 +55,7 @@ struct SplitArgs {
     int below_round = 0;
     // 0: split kernel then combine; 1: split kernel only; 2: combine only.
     int phase = 0;
+    int32_t chunk_log2;  // log2 of the instantiation's split size; set by the launcher
 };
 
 // Decode (rows = 1) and verify (rows = 8): split kernel + fixed-order combine.
@@ -135,6 +140,7 @@ struct TreeArgs {
     int32_t* vtable;  // out: [n_seq * rows][max_pages]
     int32_t* vlens;   // out: [n_seq * rows]
     int32_t* vfloor;  // out: [n_seq * rows], first key of the split holding C - rows
+    int32_t chunk;    // split size of the decode kernels that read the views
 };
 hipError_t launch_tree_stage(const TreeArgs& a, hipStream_t stream);
 

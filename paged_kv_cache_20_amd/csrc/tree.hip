@@ -15,7 +15,7 @@
 // land in it) and of the next page if the branch spills into it, written to
 // two caller-reserved pool pages, a block-table row that is the sequence's
 // own up to the page before C0 and the private pages after, the view's length
-// and the first key of the 512-key split holding C0.  The decode kernels then
+// and the first key of the split holding C0.  The decode kernels then
 // run over the views (the splits below C0's on the sequence's own pages for
 // all rows at once, C0's split and the next per view, then one combine per
 // view), so a row's arithmetic is exactly the decode's.  Bytes are copied, never
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void tree_stage_kernel(TreeArgs a)
     }
     if (threadIdx.x == 0) {
         a.vlens[sr] = ok ? L : 0;
-        a.vfloor[sr] = ok ? (C0 / kChunk) * kChunk : 0;
+        a.vfloor[sr] = ok ? (C0 / a.chunk) * a.chunk : 0;
     }
     if (!ok)
         return;

@@ -64,8 +64,8 @@ def test_batch_above_the_limit_is_refused():
 
 @pytest.mark.parametrize("fp8", [True, False])
 def test_long_context_many_split_groups(fp8):
-    """257 splits of 512 keys: the combine's max and sums run over five
-    groups of 64 splits."""
+    """131,109 keys: 129 splits of 1024 keys (fp8) or 257 of 512 (bf16), so
+    the combine's max and sums run over three or five groups of 64 splits."""
     w = synth.listed("long_ctx_%s" % ("fp8" if fp8 else "bf16"), [131109, 70001], 1, 32, 8, 128,
                      fp8, 151)
     say("[gpu] long context", w.name)
