@@ -127,6 +127,8 @@ struct Geo {
     static constexpr int KT = (!FP8 && D == 256) ? 16 : 32;
     // Keys per split (see decode_chunk); likewise fixed per (head_dim, dtype).
     static constexpr int CHUNK = (D == 128 && FP8) ? 1024 : 512;
+    // A lane holds one block-table entry of an item: at most 64 pages.
+    static_assert(CHUNK / 16 <= 64, "a split spans at most 64 pages");
     static constexpr int KB = KT / 16;          // 16-key blocks per tile
     static constexpr int KEYS = 4 * KB;         // keys a lane feeds to the PV product
 };

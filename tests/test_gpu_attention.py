@@ -23,14 +23,17 @@ L = synth.listed
 SMALL = [
     L("dec_bf16_d128_g4", [1, 17, 511, 513, 1500], 1, 8, 2, 128, False, 11),
     L("dec_bf16_d256_g4", [33, 600, 1024, 2100], 1, 16, 4, 256, False, 12),
-    L("dec_fp8_d128_g4", [1, 16, 100, 512, 1025, 3000], 1, 32, 8, 128, True, 13),
+    L("dec_fp8_d128_g4", [1, 16, 100, 512, 1025, 2048, 2049, 3000, 4097], 1, 32, 8, 128, True,
+      13),
     L("dec_fp8_d256_g2", [40, 700, 1600], 1, 8, 4, 256, True, 14),
     L("dec_bf16_d128_g1", [20, 530], 1, 4, 4, 128, False, 15),
     L("dec_bf16_d128_g8", [300, 1100], 1, 16, 2, 128, False, 16),
     L("dec_bf16_d128_g16", [64, 777], 1, 16, 1, 128, False, 17),
     L("dec_bf16_d128_g3", [45, 600], 1, 6, 2, 128, False, 18),
     L("ver_bf16_d256_g4", [8, 520, 1300], 8, 16, 4, 256, False, 21, kind="verify"),
-    L("ver_fp8_d128_g4", [9, 512, 515, 2000], 8, 32, 8, 128, True, 22, kind="verify"),
+    # 2052 and 2056: rounds across and at the start of a 2048-key split
+    L("ver_fp8_d128_g4", [9, 512, 515, 2000, 2052, 2056], 8, 32, 8, 128, True, 22,
+      kind="verify"),
     L("ver_bf16_d128_g8", [100, 1030], 8, 16, 2, 128, False, 23, kind="verify"),
     L("ver_bf16_d128_g1", [600], 8, 2, 2, 128, False, 24, kind="verify"),
     L("ver_fp8_d256_g2", [17, 1111], 8, 4, 2, 256, True, 25, kind="verify"),
