@@ -112,6 +112,9 @@ struct PrefillArgs {
     int qk_fp8 = 0;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The bf16-cache prefill with score and output waves (prefill_pipe.hip);
+// hipErrorNotSupported for the shapes it does not take.
+hipError_t launch_prefill_pipe(const PrefillArgs& a, hipStream_t stream);
 
 struct CheckArgs {
     const int32_t* block_table;

@@ -775,6 +775,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
             return launch_t<256, true, 1, 8, true>(a, stream);
         return hipErrorNotSupported;
     }
+    if (!a.fp8) {
+        const hipError_t e = launch_prefill_pipe(a, stream);
+        if (e != hipErrorNotSupported)
+            return e;
+    }
     if (a.head_dim == 128)
         return a.fp8 ? launch_t<128, true, 1, 8>(a, stream) : launch_t<128, false, 1, 8>(a, stream);
     if (a.head_dim == 256)
