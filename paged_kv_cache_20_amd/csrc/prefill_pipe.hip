@@ -17,34 +17,44 @@
 //                               K rows from LDS), the online softmax, and the
 //                               probabilities P^T (bf16) written to LDS in the
 //                               exact register layout of the PV operand
-//     output wave 4 + s         O^T += V^T . P^T for the same rows (V^T read
-//                               from LDS with the transposing reads, P^T read
-//                               back from LDS), rescaled when the score wave
-//                               raised a row's running maximum
-//   Each wave reads every K (or V) operand once and feeds it to two matrix
-//   instructions, one per 16-row tile, so the LDS bytes per flop are half of
-//   a one-tile-per-wave kernel's; and each SIMD hosts one wave of each role,
-//   so one wave's softmax or LDS latency overlaps the other's matrix work.
+//     output wave 4 + w         O^T += V^T . P^T for 64 rows (groups 2 (w / 2)
+//                               and 2 (w / 2) + 1) and one half of head_dim
+//                               (w % 2): V^T read from LDS with the
+//                               transposing reads, P^T read back from LDS,
+//                               rows rescaled when their score wave raised a
+//                               running maximum
+//   A score wave feeds every K operand it reads from LDS to two matrix
+//   instructions (one per 16-row tile) and an output wave every V operand to
+//   four, so the LDS bytes per flop are a half (K) and a quarter (V) of a
+//   one-tile-per-wave kernel's; and each SIMD hosts one wave of each role, so
+//   one wave's softmax or LDS latency overlaps the other's matrix work.
 //   Roles run one tile apart: in iteration i the score waves turn tile i's
 //   scores into probabilities while the output waves accumulate tile i - 1;
 //   one barrier per iteration hands P, the rescale factors and the freshly
-//   loaded tiles over.  The score waves are software-pipelined themselves:
-//   the scores of tile i + 1 are computed on the matrix unit while tile i's
-//   exponentials run.
+//   loaded tiles over.  Each role is also pipelined by itself: a score wave
+//   computes the scores of tile i + 2 on the matrix unit while tile i's
+//   softmax runs (so the softmax never waits for products queued in the
+//   matrix unit behind the output wave's), and an output wave reads tile i's
+//   V operands while it multiplies tile i - 1's.
 //
 // Tiles and buffers
-//   Keys stream in 32-key tiles (two 16-token pages).  In iteration i the
-//   score waves read K(i + 1) and load K(i + 2) into the buffer K(i) left
-//   free; the output waves read V(i - 1) and load V(i); P and the rescale
-//   factors of tiles i - 1 and i sit in two more buffers.  Each wave loads 8
-//   key rows of one page per tile, by buffer loads that write LDS
-//   directly.  The buffer descriptor of each page covers only its rows below
-//   ctx_len, so rows past the context arrive as zeros; a block-table entry
-//   outside the pool is never dereferenced and turns the workgroup's rows to
-//   NaN.  Pages wholly below the first key any row attends are not read.
-//   K and V rows are stored row-major (bf16), each row's 16-byte chunks
-//   XOR-swizzled by the row index, so the operand reads of a column of rows
-//   are conflict-free.
+//   Keys stream in 32-key tiles (two 16-token pages) through four LDS slots
+//   per tensor.  In iteration i the score waves read K(i + 2) and load
+//   K(i + 5) into the slot K(i + 1) left free; the output waves read V(i)
+//   and load V(i + 3) into the slot V(i - 1) left free; so every tile load
+//   has two iterations to land and the per-tile barrier waits only for
+//   loads issued before the previous iteration.  P and the rescale factors
+//   of tiles i - 1 and i sit in two more buffers.  Each wave loads 8 key
+//   rows of one page per tile, by buffer loads that write LDS directly,
+//   interleaved with its matrix instructions so the workgroup's waves do not
+//   queue at the texture addresser together; block-table entries are read
+//   with scalar loads.  The buffer descriptor of each page covers only its
+//   rows below ctx_len, so rows past the context arrive as zeros; a
+//   block-table entry outside the pool is never dereferenced and turns the
+//   workgroup's rows to NaN.  Pages wholly below the first key any row
+//   attends are not read.  K and V rows are stored row-major (bf16), each
+//   row's 16-byte chunks XOR-swizzled by the row index, so the operand
+//   reads of a column of rows are conflict-free.
 //
 // Softmax
 //   A row's 8 scores of a tile sit in the 4 lanes n, n + 16, n + 32, n + 48
@@ -123,13 +133,36 @@ struct PGeo {
     static_assert(LINS * RPI == LROWS, "a wave's rows fill whole loads");
 };
 
-// A loop phase known at compile time (the tile index mod 3 selects the K and
+// A loop phase known at compile time (the tile index mod 4 selects the K and
 // V slots, so each slot is its own LDS array and the compiler can tell the
-// tile loads in flight from the reads of another slot).
+// tile loads in flight from the reads of another slot; mod 2 it selects the
+// score wave's register set).
 template <int N>
 struct Ph {
     static constexpr int v = N;
 };
+
+template <int Q, class T>
+__device__ __forceinline__ T& pick(T& a, T& b)
+{
+    if constexpr (Q == 0)
+        return a;
+    else
+        return b;
+}
+
+template <int Q, class T>
+__device__ __forceinline__ T& pick4(T& a, T& b, T& c, T& d)
+{
+    if constexpr (Q % 4 == 0)
+        return a;
+    else if constexpr (Q % 4 == 1)
+        return b;
+    else if constexpr (Q % 4 == 2)
+        return c;
+    else
+        return d;
+}
 
 // Shared state of one workgroup besides the K and V slots.
 template <int D>
@@ -147,28 +180,28 @@ struct Seq {
     int lo;    // first key any row of the workgroup attends (window / floor)
     int kh, Hk;
     int64_t n_pages;
-    __amdgpu_buffer_rsrc_t rbt;  // the sequence's block-table row, ceil(kend / 16) entries
+    const __attribute__((address_space(4))) int32_t* bt;  // the sequence's block-table row
 };
 
 // Block-table entry of the page holding key0 .. key0 + 15 (0 past the
-// workgroup's pages; load_rows decides whether the page is read).  Always one
-// bounds-checked load, so every iteration issues the same number of loads;
-// nothing here consumes the value, so its wait comes at its use.
+// workgroup's pages; prep_rows decides whether the page is read).  A scalar
+// load: the vector memory path is left to the tile loads.
 __device__ __forceinline__ int fetch_page(const Seq& b, int key0)
 {
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(b.rbt, (uint32_t)(key0 >> 4) * 4u, 0, 0);
+    const int k = __builtin_amdgcn_readfirstlane(key0);
+    int v = 0;
+    if (k < b.kend)
+        v = b.bt[k >> 4];
+    return v;
 }
 
-// This wave's 8 key rows of one tensor's tile (one page), copied to LDS by
-// buffer loads that write LDS directly.  key0: the page's first key; prow:
-// the wave's first row in the page (0 or 8); dst: the page's first row in
-// the tile's LDS buffer.  A page the workgroup does not read gets a
-// descriptor of no rows: the loads are still issued (zeros), so the count
-// per iteration is fixed.
+// The descriptor of this wave's 8 key rows of one tensor's tile (one page):
+// it covers the page's rows below ctx_len, or no rows for a page the
+// workgroup does not read (the loads are still issued and read zeros, so
+// the count per iteration is fixed).  key0: the page's first key.
 template <int D>
-__device__ __forceinline__ void load_rows(char* dst, const uint8_t* pool, const Seq& b, int key0,
-                                          int prow, int raw, const int (&loff)[PGeo<D>::LINS],
-                                          int* bad)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t prep_rows(const uint8_t* pool, const Seq& b,
+                                                            int key0, int raw, int* bad)
 {
     using G = PGeo<D>;
     const int p = __builtin_amdgcn_readfirstlane(raw);
@@ -182,13 +215,47 @@ __device__ __forceinline__ void load_rows(char* dst, const uint8_t* pool, const 
         }
     }
     const int64_t base = ((int64_t)pg * b.Hk + b.kh) * 16 * G::ROWL;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(pool + base), (short)0, rows * G::ROWL,
-                                          kRsrcFlags);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(pool + base), (short)0, rows * G::ROWL,
+                                             kRsrcFlags);
+}
+
+// Load instruction j of this wave's rows (RPI rows, 1 KiB), a buffer load
+// that writes LDS directly.  dst: the page's first row in the tile's LDS
+// buffer; prow: the wave's first row in the page (0 or 8).
+template <int D>
+__device__ __forceinline__ void issue_row(__amdgpu_buffer_rsrc_t rs, char* dst, int prow,
+                                          const int (&loff)[PGeo<D>::LINS], int j)
+{
+    using G = PGeo<D>;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (LDS void*)(dst + (prow + j * G::RPI) * G::ROWL), 16, loff[j], 0, 0, 0);
+}
+
+// All of this wave's rows of one tensor's tile (prologue).
+template <int D>
+__device__ __forceinline__ void load_rows(char* dst, const uint8_t* pool, const Seq& b, int key0,
+                                          int prow, int raw, const int (&loff)[PGeo<D>::LINS],
+                                          int* bad)
+{
+    const __amdgpu_buffer_rsrc_t rs = prep_rows<D>(pool, b, key0, raw, bad);
 #pragma unroll
-    for (int i = 0; i < G::LINS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (LDS void*)(dst + (prow + i * G::RPI) * G::ROWL), 16, loff[i], 0, 0, 0);
+    for (int j = 0; j < PGeo<D>::LINS; ++j)
+        issue_row<D>(rs, dst, prow, loff, j);
+}
+
+// Scheduling groups that spread an iteration's NL tile loads evenly among
+// its NM matrix instructions (NM / NL matrix instructions, then one load,
+// and so on), so the eight waves of a workgroup do not queue at the texture
+// addresser at the same moment.  Instructions outside the groups (LDS
+// reads, vector ALU) are scheduled freely around them.
+template <int NL, int NM>
+__device__ __forceinline__ void spread_loads()
+{
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM / NL, 0);  // matrix instructions
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // one vector-memory read
+    }
 }
 
 // The per-tile barrier.  Every LDS access of this wave is complete
@@ -216,17 +283,19 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
     __shared__ __attribute__((aligned(1024))) char s_k0[G::TILEB];
     __shared__ __attribute__((aligned(1024))) char s_k1[G::TILEB];
     __shared__ __attribute__((aligned(1024))) char s_k2[G::TILEB];
+    __shared__ __attribute__((aligned(1024))) char s_k3[G::TILEB];
     __shared__ __attribute__((aligned(1024))) char s_v0[G::TILEB];
     __shared__ __attribute__((aligned(1024))) char s_v1[G::TILEB];
     __shared__ __attribute__((aligned(1024))) char s_v2[G::TILEB];
+    __shared__ __attribute__((aligned(1024))) char s_v3[G::TILEB];
     __shared__ __attribute__((aligned(1024))) Smem<D> sm;
     auto kslot = [&](auto ph) -> char* {
-        constexpr int P = decltype(ph)::v % 3;
-        return P == 0 ? s_k0 : P == 1 ? s_k1 : s_k2;
+        constexpr int P = decltype(ph)::v % 4;
+        return P == 0 ? s_k0 : P == 1 ? s_k1 : P == 2 ? s_k2 : s_k3;
     };
     auto vslot = [&](auto ph) -> char* {
-        constexpr int P = decltype(ph)::v % 3;
-        return P == 0 ? s_v0 : P == 1 ? s_v1 : s_v2;
+        constexpr int P = decltype(ph)::v % 4;
+        return P == 0 ? s_v0 : P == 1 ? s_v1 : P == 2 ? s_v2 : s_v3;
     };
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -280,8 +349,7 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
     b.kh = kh;
     b.Hk = Hk;
     b.n_pages = a.n_pages;
-    b.rbt = __builtin_amdgcn_make_buffer_rsrc((void*)bt, (short)0,
-                                              (int)(((b.kend + 15) >> 4) * 4), kRsrcFlags);
+    b.bt = (const __attribute__((address_space(4))) int32_t*)bt;
 
     // The group's rows: wave grp's lane n, row tile rt holds workgroup row
     // 16 (2 grp + rt) + n.
@@ -307,9 +375,10 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
     // every tile of its tensor (K for the score waves, V for the output
     // waves).  Instruction i writes LDS rows prow + i RPI .. + RPI - 1 of the
     // page linearly; lane l of it fetches logical chunk pc ^ swz(row) of row
-    // rr, so the tile ends up swizzled.  Each wave issues one table load and
-    // then G::LINS tile loads per iteration, so "all but this iteration's
-    // tile loads done" is vmcnt <= G::LINS.
+    // rr, so the tile ends up swizzled.  Each wave issues G::LINS tile loads
+    // per iteration (table entries are scalar loads); a tile's loads have two
+    // iterations to land, so "all but the last two iterations' loads done"
+    // is vmcnt <= 2 G::LINS.
     const int lpage = (wave >> 1) & 1, prow = 8 * (wave & 1);
     const int pr0 = 16 * lpage;  // the wave's page's first row in a tile
     int loff[G::LINS];
@@ -321,23 +390,33 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
             loff[i] = r * G::ROWL + ((pc ^ swz(r)) * 16);
         }
     }
-    constexpr int kInFlight = G::LINS;
+    constexpr int kInFlight = 2 * G::LINS;
 
-    // Prologue: K(0..2) (score waves) and V(0) (output waves), and the table
-    // entry of the next tile each role loads (K(3), V(1)), all landed.
+    // Prologue: K(0..3) (score waves) and V(0..2) (output waves), and the
+    // table entries of the next two tiles each role loads (K(4), K(5);
+    // V(3), V(4)), all landed.  (K(4) is loaded once the score waves have
+    // read K(0).)
     const int k0 = ts * kKT + pr0;  // the wave's page's first key in tile ts
     const bool score = wave < 4;
-    int raw_next;
+    int raw0, raw1;
     if (score) {
         load_rows<D>(s_k0 + pr0 * G::ROWL, kp, b, k0, prow, fetch_page(b, k0), loff, &bad);
         load_rows<D>(s_k1 + pr0 * G::ROWL, kp, b, k0 + kKT, prow, fetch_page(b, k0 + kKT), loff,
                      &bad);
         load_rows<D>(s_k2 + pr0 * G::ROWL, kp, b, k0 + 2 * kKT, prow,
                      fetch_page(b, k0 + 2 * kKT), loff, &bad);
-        raw_next = fetch_page(b, k0 + 3 * kKT);
+        load_rows<D>(s_k3 + pr0 * G::ROWL, kp, b, k0 + 3 * kKT, prow,
+                     fetch_page(b, k0 + 3 * kKT), loff, &bad);
+        raw0 = fetch_page(b, k0 + 4 * kKT);
+        raw1 = fetch_page(b, k0 + 5 * kKT);
     } else {
         load_rows<D>(s_v0 + pr0 * G::ROWL, vp, b, k0, prow, fetch_page(b, k0), loff, &bad);
-        raw_next = fetch_page(b, k0 + kKT);
+        load_rows<D>(s_v1 + pr0 * G::ROWL, vp, b, k0 + kKT, prow, fetch_page(b, k0 + kKT), loff,
+                     &bad);
+        load_rows<D>(s_v2 + pr0 * G::ROWL, vp, b, k0 + 2 * kKT, prow,
+                     fetch_page(b, k0 + 2 * kKT), loff, &bad);
+        raw0 = fetch_page(b, k0 + 3 * kKT);
+        raw1 = fetch_page(b, k0 + 4 * kKT);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -386,25 +465,34 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
                 }
             }
         };
-        // Software pipeline: iteration i computes the scores of tile i + 1
-        // on the matrix unit while tile i's exponentials run (s holds tile i).
-        f32x4 s[kRT][2];
-        scores(s_k0, s);
-        // Iteration 0 loads K(3) into K(0)'s slot: every score wave must have
-        // read K(0) first (the output waves take this barrier before their
+        // Software pipeline, two tiles deep: iteration i computes the scores
+        // of tile i + 2 on the matrix unit while tile i's softmax runs, so the
+        // softmax never waits for products still queued in the matrix unit
+        // behind the output wave's.  The scores of tile t live in s0..s3
+        // (t mod 4).
+        f32x4 s0[kRT][2], s1[kRT][2], s2[kRT][2], s3[kRT][2];
+        scores(s_k0, s0);
+        scores(s_k1, s1);
+        // K(4) goes into K(0)'s slot: every score wave must have read K(0)
+        // and K(1) first (the output waves take this barrier before their
         // loop).
         __syncthreads();
-        int rawk = raw_next;  // K(3)'s page
-        // Iteration i, phase P = i mod 3.
+        load_rows<D>(s_k0 + pr0 * G::ROWL, kp, b, k0 + 4 * kKT, prow, raw0, loff, &bad);
+        raw0 = raw1;
+        raw1 = fetch_page(b, k0 + 6 * kKT);
+        // Iteration i, phase P = i mod 4.
         auto body = [&](int i, auto ph) {
             constexpr int P = decltype(ph)::v;
-            // K(i + 3) into the slot K(i) held (read last in iteration i - 1);
-            // its table entry was fetched before K(i + 2)'s loads were issued,
-            // so waiting for it does not wait for them.
-            const int rawn = fetch_page(b, k0 + (i + 4) * kKT);
-            load_rows<D>(kslot(Ph<P>()) + pr0 * G::ROWL, kp, b, k0 + (i + 3) * kKT, prow, rawk,
-                         loff, &bad);
-            rawk = rawn;
+            auto& s = pick4<P>(s0, s1, s2, s3);       // tile i
+            auto& sn = pick4<P + 2>(s0, s1, s2, s3);  // tile i + 2
+            // K(i + 5) goes into the slot K(i + 1) held (read last in
+            // iteration i - 1); its table entry was fetched two iterations ago,
+            // the entry of K(i + 7) is fetched now.
+            const __amdgpu_buffer_rsrc_t rl =
+                prep_rows<D>(kp, b, k0 + (i + 5) * kKT, raw0, &bad);
+            char* kdst = kslot(Ph<P + 1>()) + pr0 * G::ROWL;
+            raw0 = raw1;
+            raw1 = fetch_page(b, k0 + (i + 7) * kKT);
             if (i < T) {
                 const int buf = i & 1;
                 const int tile0 = (ts + i) * kKT;
@@ -462,12 +550,11 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
                 if (lane == 0)
                     sm.flag[buf][grp] = any ? 1 : 0;
 
-                // The scores of tile i + 1 (stale K past the last tile: never
+                // The scores of tile i + 2 (stale K past the last tile: never
                 // used), issued beside tile i's probabilities, this lane's part
                 // of the row sums, and the P^T operand: k index j of the 32-key
                 // step is key 16 (j / 4) + 4 kb + j % 4, matching the V^T reads.
-                f32x4 sn[kRT][2];
-                scores(kslot(Ph<P + 1>()), sn);
+                scores(kslot(Ph<P + 2>()), sn);
 #pragma unroll
                 for (int rt = 0; rt < kRT; ++rt) {
                     const float mu = m[rt] == neg_inf() ? 0.f : m[rt];
@@ -486,22 +573,28 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
                     pw[3] = pack_bf16(e[1][2], e[1][3]);
                     sm.p[buf][grp][rt][lane] = pw;
                 }
+                // The tile loads, spread among the matrix instructions.
 #pragma unroll
-                for (int rt = 0; rt < kRT; ++rt)
+                for (int j = 0; j < G::LINS; ++j)
+                    issue_row<D>(rl, kdst, prow, loff, j);
+                spread_loads<G::LINS, 4 * G::KSTEPS>();
+            } else {
 #pragma unroll
-                    for (int kq = 0; kq < 2; ++kq)
-                        s[rt][kq] = sn[rt][kq];
+                for (int j = 0; j < G::LINS; ++j)
+                    issue_row<D>(rl, kdst, prow, loff, j);
             }
-            // K(i + 2) (issued in iteration i - 1) has landed; K(i + 3) may
-            // still be in flight.
+            // K(i + 3) (issued in iteration i - 2) has landed; K(i + 4) and
+            // K(i + 5) may still be in flight.
             tile_barrier<kInFlight>();
         };
-        for (int i = 0; i <= T; i += 3) {
+        for (int i = 0; i <= T; i += 4) {
             body(i, Ph<0>());
             if (i + 1 <= T)
                 body(i + 1, Ph<1>());
             if (i + 2 <= T)
                 body(i + 2, Ph<2>());
+            if (i + 3 <= T)
+                body(i + 3, Ph<3>());
         }
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
@@ -514,77 +607,103 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     } else {
-        // ---- output wave: O^T += V^T . P^T, one tile behind.
-        constexpr int VBS = G::DBLK < 8 ? G::DBLK : 8;
-        int voff[VBS];
+        // ---- output wave: O^T += V^T . P^T, one tile behind, for 64 rows
+        // (the row groups 2 rh and 2 rh + 1) and one half of head_dim (dh):
+        // each V operand read feeds four 16-row tiles.
+        const int ow = wave - 4, rh = ow >> 1, dh = ow & 1;
+        constexpr int DH = G::DBLK / 2;  // d blocks of the half
+        int voff[DH];
         {
             const int vkey = 4 * kb + (n >> 2);
             const int sw = swz(vkey);
 #pragma unroll
-            for (int j = 0; j < VBS; ++j)
-                voff[j] = vkey * G::ROWL + 16 * ((2 * j + ((n & 3) >> 1)) ^ sw) + (n & 1) * 8;
+            for (int j = 0; j < DH; ++j) {
+                const int jb = dh * DH + j;
+                voff[j] = vkey * G::ROWL + 16 * ((2 * (jb & 7) + ((n & 3) >> 1)) ^ sw) +
+                          (n & 1) * 8 + 256 * (jb >> 3);
+            }
         }
-        f32x4 O[kRT][G::DBLK];
+        // Tile t of the wave: group 2 rh + t / 2, row tile t % 2.
+        f32x4 O[2 * kRT][DH];
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
+        for (int t = 0; t < 2 * kRT; ++t)
 #pragma unroll
-            for (int jb = 0; jb < G::DBLK; ++jb)
-                O[rt][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < DH; ++j)
+                O[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();  // the score waves' barrier after the tile-0 scores
-        int rawv = raw_next;  // V(1)'s page
-        // Iteration i, phase P = i mod 3: V(i + 1) goes to slot P + 1, V(i - 1)
-        // is read from slot P + 2 (mod 3).
+        // Iteration i, phase P = i mod 4: the products of tile i - 1 with V
+        // operands read in iteration i - 1 (va, ping-pong by parity), the V
+        // operands of tile i read from slot P, and V(i + 3) loaded into slot
+        // P + 3, which V(i - 1) left free.
+        u32x4 vaA[DH], vaB[DH];
         auto body = [&](int i, auto ph) {
             constexpr int P = decltype(ph)::v;
-            // V(i + 1) into the slot V(i - 2) held (read last in iteration
-            // i - 1); table entries are fetched an iteration ahead, before the
-            // previous tile's loads.
-            const int rawn = fetch_page(b, k0 + (i + 2) * kKT);
-            load_rows<D>(vslot(Ph<P + 1>()) + pr0 * G::ROWL, vp, b, k0 + (i + 1) * kKT, prow,
-                         rawv, loff, &bad);
-            rawv = rawn;
+            auto& va = pick<(P + 1) % 2>(vaA, vaB);  // V(i - 1)
+            auto& vn = pick<P % 2>(vaA, vaB);        // V(i)
+            // V(i + 3)'s table entry was fetched two iterations ago, the entry
+            // of V(i + 5) is fetched now.
+            const __amdgpu_buffer_rsrc_t rl =
+                prep_rows<D>(vp, b, k0 + (i + 3) * kKT, raw0, &bad);
+            char* vdst = vslot(Ph<P + 3>()) + pr0 * G::ROWL;
+            raw0 = raw1;
+            raw1 = fetch_page(b, k0 + (i + 5) * kKT);
             if (i >= 1) {
                 const int buf = (i - 1) & 1;
-                if (sm.flag[buf][grp]) {
+                u32x4 pw[2 * kRT];
 #pragma unroll
-                    for (int rt = 0; rt < kRT; ++rt) {
-                        const float al = sm.alpha[buf][grp][rt][n];
+                for (int t = 0; t < 2 * kRT; ++t)
+                    pw[t] = sm.p[buf][2 * rh + (t >> 1)][t & 1][lane];
 #pragma unroll
-                        for (int jb = 0; jb < G::DBLK; ++jb)
-                            O[rt][jb] = O[rt][jb] * al;
+                for (int h = 0; h < 2; ++h) {
+                    if (sm.flag[buf][2 * rh + h]) {
+#pragma unroll
+                        for (int rt = 0; rt < kRT; ++rt) {
+                            const float al = sm.alpha[buf][2 * rh + h][rt][n];
+#pragma unroll
+                            for (int j = 0; j < DH; ++j)
+                                O[2 * h + rt][j] = O[2 * h + rt][j] * al;
+                        }
                     }
                 }
-                u32x4 pw[kRT];
 #pragma unroll
-                for (int rt = 0; rt < kRT; ++rt)
-                    pw[rt] = sm.p[buf][grp][rt][lane];
-                const char* vr = vslot(Ph<P + 2>());
+                for (int j = 0; j < DH; ++j)
 #pragma unroll
-                for (int jb = 0; jb < G::DBLK; ++jb) {
-                    const char* v0 = vr + voff[jb % VBS] + 256 * (jb / VBS);
+                    for (int t = 0; t < 2 * kRT; ++t)
+                        O[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, va[j]), __builtin_bit_cast(bf16x8, pw[t]),
+                            O[t][j], 0, 0, 0);
+            }
+            if (i < T) {
+                const char* vr = vslot(Ph<P>());
+#pragma unroll
+                for (int j = 0; j < DH; ++j) {
+                    const char* v0 = vr + voff[j];
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)v0);
                     const s16x4 hi =
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(v0 + 16 * G::ROWL));
                     const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
                     const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                    const u32x4 va = u32x4{l2[0], l2[1], h2[0], h2[1]};
-#pragma unroll
-                    for (int rt = 0; rt < kRT; ++rt)
-                        O[rt][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pw[rt]),
-                            O[rt][jb], 0, 0, 0);
+                    vn[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
                 }
             }
-            // V(i) (issued in iteration i - 1) has landed; V(i + 1) may still
-            // be in flight.
+            // The tile loads, spread among the matrix instructions.
+#pragma unroll
+            for (int j = 0; j < G::LINS; ++j)
+                issue_row<D>(rl, vdst, prow, loff, j);
+            if (i >= 1)
+                spread_loads<G::LINS, 2 * kRT * DH>();
+            // V(i + 1) (issued in iteration i - 2) has landed; V(i + 2) and
+            // V(i + 3) may still be in flight.
             tile_barrier<kInFlight>();
         };
-        for (int i = 0; i <= T; i += 3) {
+        for (int i = 0; i <= T; i += 4) {
             body(i, Ph<0>());
             if (i + 1 <= T)
                 body(i + 1, Ph<1>());
             if (i + 2 <= T)
                 body(i + 2, Ph<2>());
+            if (i + 3 <= T)
+                body(i + 3, Ph<3>());
         }
         if (bad)
             sm.bad = 1;
@@ -592,17 +711,21 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
         __syncthreads();
         const bool nan = sm.bad != 0;
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-            if (row[rt] >= n_rows)
+        for (int t = 0; t < 2 * kRT; ++t) {
+            const int wrow = 16 * (2 * kRT * rh + t) + n;  // row in the workgroup
+            const int hg = wrow / BP, p = wrow - hg * BP;
+            const int r = pb * BP + p;
+            if (r >= n_rows)
                 continue;
-            const float inv = 1.f / sm.lsum[grp][rt][n];
-            uint16_t* out = (uint16_t*)a.out + ((tok0 + row[rt]) * H + head[rt]) * D;
+            const int hd = kh * g + hg;
+            const float inv = 1.f / sm.lsum[2 * rh + (t >> 1)][t & 1][n];
+            uint16_t* out = (uint16_t*)a.out + ((tok0 + r) * H + hd) * D;
 #pragma unroll
-            for (int jb = 0; jb < G::DBLK; ++jb) {
-                const int d = 16 * jb + 4 * kb;
+            for (int j = 0; j < DH; ++j) {
+                const int d = 16 * (dh * DH + j) + 4 * kb;
                 u32x2 o;
-                o[0] = nan ? 0x7FC07FC0u : pack_bf16(O[rt][jb][0] * inv, O[rt][jb][1] * inv);
-                o[1] = nan ? 0x7FC07FC0u : pack_bf16(O[rt][jb][2] * inv, O[rt][jb][3] * inv);
+                o[0] = nan ? 0x7FC07FC0u : pack_bf16(O[t][j][0] * inv, O[t][j][1] * inv);
+                o[1] = nan ? 0x7FC07FC0u : pack_bf16(O[t][j][2] * inv, O[t][j][3] * inv);
                 *(u32x2*)(out + d) = o;
             }
         }
