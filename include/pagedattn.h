@@ -13,9 +13,13 @@
  * ---------------------------------------
  *  - Pointers are DEVICE pointers unless the argument name ends in `_host`.
  *    The caller allocates and owns every buffer, including the workspace;
- *    the library allocates no device memory and keeps no state between
- *    calls apart from a per-thread error string and a per-device launch
- *    shape it reads once from the driver.
+ *    the library allocates no device memory at run time.  State kept
+ *    between calls: a per-thread error string; a per-device launch shape
+ *    read once from the driver; the scratch array of
+ *    attn_paged_decode_noalloc (part of the library's device code, one per
+ *    GPU) and its address per GPU; and the two measurement hooks at the end
+ *    of this header (a per-thread event pair consumed by the next call, and
+ *    a process-wide grid bound that is 0, i.e. off, unless set).
  *  - Device work is enqueued on `stream` and is asynchronous: inputs must
  *    stay unchanged and outputs unread until the stream has passed the call.
  *    Outputs never alias inputs.
@@ -147,6 +151,30 @@ int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
  * the same cache.  Needs ctx_lens[s] >= 8 and, besides the decode limits,
  * ceil(8 / floor(16 / g)) * head_dim <= 512 with g = n_head / n_head_kv.
  */
+/*
+ * attn_paged_decode_noalloc -- attn_paged_decode without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * The split partials go to a scratch array inside the library (64 MiB, one
+ * per GPU the library runs on, held until the process ends); the call makes
+ * no allocation of any kind.  The caller still passes every input and the
+ * output.  Arguments, limits and results are those of attn_paged_decode
+ * (the same kernels: every output row is bit for bit attn_paged_decode's),
+ * and additionally the call's partials,
+ * attn_paged_workspace_bytes(0, n_seq, max_pages_per_seq, n_head, head_dim)
+ * bytes, must fit the scratch array, else ATTN_E_WORKSPACE and nothing is
+ * written.  All calls on one GPU share the array: calls that may overlap on
+ * a GPU (several streams, several threads) race and must be serialised by
+ * the caller.  Nothing in the array needs clearing between calls.
+ */
+int attn_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale, int64_t n_pages,
+                              const int32_t* block_table, int32_t max_pages_per_seq,
+                              const int32_t* ctx_lens, int32_t n_seq, int32_t n_head,
+                              int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                              attn_kv_dtype kv_dtype, void* out, hipStream_t stream);
+
 int attn_paged_verify(const void* q, const void* k_pool, const void* v_pool,
                       const float* k_scale, const float* v_scale, int64_t n_pages,
                       const int32_t* block_table, int32_t max_pages_per_seq,

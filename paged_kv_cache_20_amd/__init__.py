@@ -15,7 +15,8 @@ _API = {
     "VERIFY_ROWS", "AttnError", "attn_block_table_build", "attn_caps",
     "attn_check_block_table_host", "attn_check_device", "attn_check_lengths_host",
     "attn_kv_append",
-    "attn_last_error", "attn_paged_decode", "attn_paged_decode_window", "attn_paged_mixed",
+    "attn_last_error", "attn_paged_decode", "attn_paged_decode_noalloc", "attn_paged_decode_window",
+    "attn_paged_mixed",
     "attn_paged_prefill", "attn_paged_prefill_fp8", "attn_paged_prefill_window",
     "attn_paged_verify", "attn_paged_verify_tree", "attn_paged_verify_width",
     "attn_paged_workspace_bytes", "attn_set_kernel_timer", "attn_set_max_workgroups", "lib",

@@ -33,7 +33,8 @@ ATTN_E_RANGE = -5
 ATTN_E_DEVICE = -6
 
 EXPORTS = [
-    "attn_paged_decode", "attn_paged_verify", "attn_paged_verify_width",
+    "attn_paged_decode", "attn_paged_decode_noalloc", "attn_paged_verify",
+    "attn_paged_verify_width",
     "attn_paged_verify_tree", "attn_paged_prefill", "attn_paged_prefill_fp8",
     "attn_paged_mixed", "attn_paged_decode_window", "attn_paged_prefill_window",
     "attn_kv_append", "attn_block_table_build", "attn_paged_workspace_bytes", "attn_caps",
@@ -64,6 +65,8 @@ _SPLIT_ARGS = [_P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _
                _P, _P, _SZ, _P]
 _lib.attn_paged_decode.argtypes = _SPLIT_ARGS
 _lib.attn_paged_decode.restype = ctypes.c_int
+_lib.attn_paged_decode_noalloc.argtypes = _SPLIT_ARGS[:-3] + [_P]
+_lib.attn_paged_decode_noalloc.restype = ctypes.c_int
 _lib.attn_paged_verify.argtypes = _SPLIT_ARGS
 _lib.attn_paged_verify.restype = ctypes.c_int
 _lib.attn_paged_verify_width.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32,
@@ -167,6 +170,15 @@ def attn_paged_decode(q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
     return _split(_lib.attn_paged_decode, q, k_pool, v_pool, k_scale, v_scale, n_pages,
                   block_table, max_pages_per_seq, ctx_lens, n_seq, n_head, n_head_kv, head_dim,
                   page_size, kv_dtype, out, workspace, workspace_bytes, stream)
+
+
+def attn_paged_decode_noalloc(q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                              max_pages_per_seq, ctx_lens, n_seq, n_head, n_head_kv, head_dim,
+                              page_size, kv_dtype, out, stream=None):
+    return _check(_lib.attn_paged_decode_noalloc(
+        _dp(q), _dp(k_pool), _dp(v_pool), _dp(k_scale), _dp(v_scale), n_pages,
+        _dp(block_table), max_pages_per_seq, _dp(ctx_lens), n_seq, n_head, n_head_kv, head_dim,
+        page_size, kv_dtype, _dp(out), _stream(stream)))
 
 
 def attn_paged_verify(q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,

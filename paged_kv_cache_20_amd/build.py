@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["api.cpp", "block_table.cpp", "decode.hip", "append.hip", "prefill.hip", "prefill_pipe.hip", "check.hip", "tree.hip"]
+SOURCES = ["api.cpp", "block_table.cpp", "decode.hip", "append.hip", "prefill.hip", "prefill_pipe.hip", "check.hip", "tree.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

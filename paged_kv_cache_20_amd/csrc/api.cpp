@@ -151,7 +151,8 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
                int32_t n_seq, int32_t n_head, int32_t n_head_kv, int32_t head_dim,
                int32_t page_size, attn_kv_dtype kv_dtype, void* out, void* workspace,
                size_t workspace_bytes, hipStream_t stream, int32_t window = 0,
-               const int32_t* kv_floor = nullptr, int below_round = 0, int phase = 0)
+               const int32_t* kv_floor = nullptr, int below_round = 0, int phase = 0,
+               bool noalloc = false)
 {
     int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                           max_pages, n_head, n_head_kv, head_dim, page_size, kv_dtype, out);
@@ -180,6 +181,18 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     if (((int64_t)(rows - 1) * ms * n_head + n_head) * head_dim * 4 >= ((int64_t)1 << 31))
         return fail(ATTN_E_UNSUPPORTED, "%s: rows x splits x heads too large", fn);
     const size_t need = split_ws_bytes(rows, n_seq, max_pages, n_head, head_dim);
+    if (noalloc) {
+        // The partials go to the library's per-device scratch array.
+        if (need > pa::kScratchBytes)
+            return fail(ATTN_E_WORKSPACE,
+                        "%s: the call needs %zu bytes of split partials; the scratch array "
+                        "holds %zu (call attn_paged_decode with a workspace)",
+                        fn, need, pa::kScratchBytes);
+        rc = from_hip(pa::scratch_address(&workspace), fn);
+        if (rc != ATTN_OK)
+            return rc;
+        workspace_bytes = pa::kScratchBytes;
+    }
     rc = check_workspace(fn, workspace, workspace_bytes, need);
     if (rc != ATTN_OK)
         return rc;
@@ -304,6 +317,19 @@ int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
     return split_call("attn_paged_decode", 1, q, k_pool, v_pool, k_scale, v_scale, n_pages,
                       block_table, max_pages_per_seq, ctx_lens, n_seq, n_head, n_head_kv,
                       head_dim, page_size, kv_dtype, out, workspace, workspace_bytes, stream);
+}
+
+int attn_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale, int64_t n_pages,
+                              const int32_t* block_table, int32_t max_pages_per_seq,
+                              const int32_t* ctx_lens, int32_t n_seq, int32_t n_head,
+                              int32_t n_head_kv, int32_t head_dim, int32_t page_size,
+                              attn_kv_dtype kv_dtype, void* out, hipStream_t stream)
+{
+    return split_call("attn_paged_decode_noalloc", 1, q, k_pool, v_pool, k_scale, v_scale,
+                      n_pages, block_table, max_pages_per_seq, ctx_lens, n_seq, n_head,
+                      n_head_kv, head_dim, page_size, kv_dtype, out, nullptr, 0, stream, 0,
+                      nullptr, 0, 0, true);
 }
 
 int attn_paged_verify(const void* q, const void* k_pool, const void* v_pool,

@@ -19,6 +19,13 @@ inline int decode_chunk(int32_t head_dim, bool fp8) { return head_dim == 128 && 
 // sequences lives in LDS).
 constexpr int kMaxSeq = 4096;
 
+// The device scratch array of the no-allocation decode entry point
+// (scratch.hip): its size, the GPUs it is tracked on, and its address on the
+// current GPU (taken once per device with hipGetSymbolAddress).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_address(void** out);
+
 inline int64_t max_splits(int32_t max_pages_per_seq, int32_t page_size)
 {
     return ((int64_t)max_pages_per_seq * page_size + kChunk - 1) / kChunk;

@@ -303,3 +303,24 @@ def test_prefill_fp8_host_checks(pa, over, code, needle):
         pa.attn_paged_prefill_fp8(**args)
     assert e.value.code == code
     assert needle in str(e.value)
+
+
+def noalloc_args(**over):
+    a = decode_args(**over)
+    del a["workspace"], a["workspace_bytes"]
+    return a
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(q=None), -1, "q is NULL"),
+    (dict(n_seq=0), -2, "zero sequences"),
+    (dict(head_dim=96), -3, "head_dim 96"),
+    # 4096 sequences x 64 splits x 8 heads x 130 floats: beyond the 64 MiB array
+    (dict(n_seq=4096, max_pages_per_seq=2048), -4, "scratch array holds"),
+])
+def test_decode_noalloc_host_checks(pa, over, code, needle):
+    with pytest.raises(pa.AttnError) as e:
+        pa.attn_paged_decode_noalloc(**noalloc_args(**over))
+    assert e.value.code == code
+    assert needle in str(e.value)
+    assert "attn_paged_decode_noalloc" in str(e.value)
