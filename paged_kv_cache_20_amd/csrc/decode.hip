@@ -600,11 +600,15 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         }
     };
     // Scales of item I's pages, lane e for page e (zero past the item, for
-    // an entry outside the pool, and for bf16).
+    // a page wholly below the item's first key -- a runtime floor may have
+    // released its entry, which may then name any page -- for an entry
+    // outside the pool, and for bf16).  A zero V scale keeps the masked keys'
+    // zero probabilities zero.
     auto load_scales = [&](float& ks, float& vs, const Item& I, int pidv, bool live) {
         ks = vs = 0.f;
         if constexpr (FP8) {
-            const bool ok = live && lane < I.npg && pidv >= 0 && (int64_t)pidv < a.n_pages;
+            const bool ok = live && lane < I.npg && I.t0 + 16 * lane + 16 > I.lo && pidv >= 0 &&
+                            (int64_t)pidv < a.n_pages;
             const uint32_t so = ok ? (uint32_t)(pidv * Hk + I.kh) * 4u : kFar;
             ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ks, so, 0, 0));
             vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_vs, so, 0, 0));

@@ -122,6 +122,40 @@ def test_released_pages_below_the_window_are_not_read(cfg):
     assert same_bits(out, ref)
 
 
+def unused_page(inp):
+    """A pool page no sequence uses (its codes, values and fp8 scales are
+    NaN)."""
+    lens = inp.lengths.cpu().numpy()
+    table = inp.table.cpu().numpy()
+    used = {int(p) for s, c in enumerate(lens) for p in table[s, :-(-int(c) // PAGE)]}
+    free = [p for p in range(inp.n_pages) if p not in used]
+    assert free
+    return free[0]
+
+
+def test_released_entries_naming_a_poisoned_page_change_nothing(cfg):
+    """Entries below every row's first key that name an in-range page whose
+    values and scales are NaN: same bits as with -1 entries (the page is
+    neither read nor its scales used)."""
+    w, inp, gpu, oc = cfg
+    window = 300
+    floor = torch.from_numpy(floors_for(inp, 8, 6)).cuda()
+    table = inp.table.clone()
+    lens = inp.lengths.cpu().numpy()
+    fl = floor.cpu().numpy()
+    poison = unused_page(inp)
+    table_m1 = inp.table.clone()
+    for s, c in enumerate(lens):
+        lo = max(int(fl[s]), int(c) - 8 - window + 1)
+        table[s, :lo // PAGE] = poison
+        table_m1[s, :lo // PAGE] = -1
+    ref = run_window(gpu, inp, inp.q, window, floor, table=table_m1)
+    out = run_window(gpu, inp, inp.q, window, floor, table=table)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    assert same_bits(out, ref)
+
+
 def test_bad_floor_gives_nan_rows_of_that_sequence_only(cfg):
     w, inp, gpu, oc = cfg
     floor = torch.zeros(inp.q.shape[0], dtype=torch.int32, device="cuda")
@@ -178,5 +212,15 @@ def test_prefill_window_parity(w, windows):
     pa.attn_paged_prefill_window(q, w.rows, gpu.k, gpu.v, gpu.ks, gpu.vs, inp.n_pages,
                                  inp.table, inp.table.shape[1], C, window, floor, w.n_head,
                                  w.n_head_kv, w.head_dim, PAGE, gpu.kv, out1)
+    # the same entries naming a page whose values are NaN
+    used = {int(p) for p in inp.table[0, :-(-C // PAGE)].cpu().numpy()}
+    poison = next(p for p in range(inp.n_pages) if p not in used)
+    table_p = inp.table.clone()
+    table_p[0, :lo // PAGE] = poison
+    out3 = torch.empty_like(q)
+    pa.attn_paged_prefill_window(q, w.rows, gpu.k, gpu.v, gpu.ks, gpu.vs, inp.n_pages, table_p,
+                                 table_p.shape[1], C, window, floor, w.n_head, w.n_head_kv,
+                                 w.head_dim, PAGE, gpu.kv, out3)
     torch.cuda.synchronize()
     assert same_bits(out2, out1)
+    assert same_bits(out3, out1)
