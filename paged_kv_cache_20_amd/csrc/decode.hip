@@ -10,9 +10,12 @@
 //   s, clipped to ctx_len, with P = 1024 for the fp8 cache at head_dim 128
 //   and 512 otherwise.  Split boundaries are absolute multiples of P,
 //   so the items a row takes part in, and everything computed inside them,
-//   depend on the row's position and its sequence's own data only.  Each wave
-//   of a persistent grid walks items (wave, wave + total waves, ...); which
-//   wave takes an item changes nothing in its arithmetic.  The block-table
+//   depend on the row's position and its sequence's own data only.  Items
+//   are listed full splits first, then the partial last splits from the
+//   longest; each wave of a persistent grid takes one item per round of the
+//   list, rounds walked in alternating directions, so the waves' shares of
+//   keys even out and the grid's last items are its shortest.  Which wave
+//   takes an item changes nothing in its arithmetic.  The block-table
 //   entries of a wave's next item are fetched while it works on the current
 //   one.
 //
@@ -407,11 +410,11 @@ __device__ __forceinline__ int key_floor(int pos, int window, int floor_s)
 }
 
 // Items are numbered full splits first (sequence, split, kv head), then the
-// partial last splits (sequence, kv head): a wave's later items are the
-// short ones, so the grid's last round is short.  s_pre / s_pp: exclusive
-// prefixes over sequences of their full / partial items.
+// partial last splits, longest first (sequence order `s_ord`, kv head).
+// s_pre: exclusive prefix over sequences of their full items; s_lo: the
+// first key each sequence's first row attends (-1: no items).
 template <int KT, int NT, int CH>
-__device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, const int* s_len,
+__device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_ord, const int* s_len,
                                              const int* s_lo, int S, int Hk, int slices,
                                              int item_in)
 {
@@ -420,23 +423,29 @@ __device__ __forceinline__ Item resolve_item(const int* s_pre, const int* s_pp, 
     const int item = item_in / slices;
     const int tau0 = (item_in - item * slices) * NT;
     const int nfull = s_pre[S];
-    const bool full = item < nfull;
-    const int* pre = full ? s_pre : s_pp;
-    const int key = full ? item : item - nfull;
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= key)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
     Item it;
-    it.s = __builtin_amdgcn_readfirstlane(lo);
-    const int local = __builtin_amdgcn_readfirstlane(key - pre[it.s]);
-    it.C = __builtin_amdgcn_readfirstlane(s_len[it.s]);
-    const int lo_s = __builtin_amdgcn_readfirstlane(s_lo[it.s]);
+    int s, local;
+    if (item < nfull) {
+        int lo = 0, hi = S - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= item)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        s = __builtin_amdgcn_readfirstlane(lo);
+        local = __builtin_amdgcn_readfirstlane(item - s_pre[s]);
+    } else {
+        const int rank = (item - nfull) / Hk;
+        s = __builtin_amdgcn_readfirstlane(s_ord[rank]);
+        local = item - nfull - rank * Hk;
+    }
+    it.s = s;
+    it.C = __builtin_amdgcn_readfirstlane(s_len[s]);
+    const int lo_s = max(__builtin_amdgcn_readfirstlane(s_lo[s]), 0);
     const int j0 = lo_s / CH;  // the sequence's first split with keys to attend
+    const bool full = item < nfull;
     it.j = full ? j0 + local / Hk : it.C / CH;
     it.kh = full ? local - (local / Hk) * Hk : local;
     // Tiles keep their absolute grid (a multiple of KT from the split start)
@@ -467,19 +476,22 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     constexpr int NBUF = Plan<D, FP8, NT>::NBUF;
     constexpr bool PREQ = Plan<D, FP8, NT>::PREQ;
     constexpr int KT = G::KT;
+    static_assert(G::CHUNK / 16 <= 64, "one lane per partial-split length class");
     __shared__ int s_pre[kMaxSeq + 1];  // full items before each sequence
-    __shared__ int s_pp[kMaxSeq + 1];   // partial items before each sequence
+    __shared__ int s_ord[kMaxSeq];      // sequences with a partial split, longest first
     __shared__ int s_len[kMaxSeq];
-    __shared__ int s_lo[kMaxSeq];  // first key the sequence's first row attends
+    __shared__ int s_lo[kMaxSeq];  // first key the sequence's first row attends, -1: none
     __shared__ int s_tmp[256], s_tmp2[256];
+    __shared__ int s_npart;  // partial items
 
     const int S = a.n_seq, R = a.rows, Hk = a.n_head_kv, H = a.n_head;
     const int g = H / Hk, ppt = 16 / g;
     const int64_t cap = (int64_t)a.max_pages * 16;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // Exclusive prefixes over sequences of their full and partial work items,
-    // and the lengths (kept in LDS: item set-up then waits on no global load).
+    // The work list, built in LDS by every workgroup alike (item set-up then
+    // waits on no global load).  Lengths, first keys and the exclusive prefix
+    // over sequences of their full items first.
     {
         // lo: first key of the sequence's first row; -1 marks a sequence
         // whose floor lies outside 0 .. that row's position (no items, NaN).
@@ -490,64 +502,108 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             return key_floor(C - R, a.window, f);
         };
         auto nfull = [&](int C, int lo) {
-            if (!ctx_ok(C, R, cap) || lo < 0)
+            if (lo < 0)
                 return 0;
             const int end = a.below_round ? (C - R) / G::CHUNK : C / G::CHUNK;
             return max(end - lo / G::CHUNK, 0) * Hk;
         };
-        auto npart = [&](int C, int lo) {
-            return ctx_ok(C, R, cap) && lo >= 0 && !a.below_round && C % G::CHUNK != 0 ? Hk
-                                                                                       : 0;
-        };
         const int per = (S + 255) / 256;
         const int b0 = tid * per;
-        int loc = 0, loc2 = 0;
+        int loc = 0;
         for (int i = 0; i < per; ++i) {
             const int s = b0 + i;
             if (s < S) {
                 const int C = a.ctx_lens[s];
                 const int lo = ctx_ok(C, R, cap) ? first_key(s, C) : -1;
+                s_len[s] = C;
+                s_lo[s] = lo;
                 loc += nfull(C, lo);
-                loc2 += npart(C, lo);
             }
         }
         s_tmp[tid] = loc;
-        s_tmp2[tid] = loc2;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
             const int v = tid >= off ? s_tmp[tid - off] : 0;
-            const int v2 = tid >= off ? s_tmp2[tid - off] : 0;
             __syncthreads();
             s_tmp[tid] += v;
-            s_tmp2[tid] += v2;
             __syncthreads();
         }
         int run = tid ? s_tmp[tid - 1] : 0;
-        int run2 = tid ? s_tmp2[tid - 1] : 0;
         for (int i = 0; i < per; ++i) {
             const int s = b0 + i;
             if (s < S) {
                 s_pre[s] = run;
-                s_pp[s] = run2;
-                const int C = a.ctx_lens[s];
-                const int lo = ctx_ok(C, R, cap) ? first_key(s, C) : -1;
-                s_len[s] = C;
-                s_lo[s] = max(lo, 0);
-                run += nfull(C, lo);
-                run2 += npart(C, lo);
+                run += nfull(s_len[s], s_lo[s]);
             }
         }
-        if (tid == 255) {
+        if (tid == 255)
             s_pre[S] = s_tmp[255];
-            s_pp[S] = s_tmp2[255];
-        }
         __syncthreads();
     }
+    // Then the order of the partial last splits: by length class (pages,
+    // 1 .. CHUNK/16) from the longest, and by sequence within a class (a
+    // stable counting sort).  With full items first and each wave taking
+    // the items of rounds in alternating directions, the longest partial
+    // items go to the waves with the least work, and the last items of the
+    // grid are the shortest.
+    {
+        // Length class of sequence s's partial split (0: it has none).
+        auto pclass = [&](int s) {
+            const int C = s_len[s], lo = s_lo[s];
+            if (a.below_round || lo < 0 || C % G::CHUNK == 0)
+                return 0;
+            return (C - max(lo, C - C % G::CHUNK) + 15) >> 4;
+        };
+        // s_tmp[0, 64): sequences per class; [64, 128): placed so far;
+        // [128, 192): sequences of longer classes.  Class c is entry c - 1.
+        if (tid < 64)
+            s_tmp[tid] = s_tmp[64 + tid] = 0;
+        __syncthreads();
+        for (int s = tid; s < S; s += 256) {
+            const int c = pclass(s);
+            if (c > 0)
+                atomicAdd(&s_tmp[c - 1], 1);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            int longer = 0;
+            for (int c = tid + 1; c < 64; ++c)
+                longer += s_tmp[c];
+            s_tmp[128 + tid] = longer;
+            if (tid == 0)
+                s_npart = (longer + s_tmp[0]) * Hk;
+        }
+        __syncthreads();
+        for (int s0 = 0; s0 < S; s0 += 256) {
+            const int s = s0 + tid;
+            const int c = s < S ? pclass(s) : 0;
+            // Lanes below with the same class; lanes of the wave in class lane + 1.
+            int below = 0, mine = 0;
+            for (int j = 0; j < 64; ++j) {
+                const int cj = rdlane(c, j);
+                below += (j < lane && cj == c) ? 1 : 0;
+                mine += cj == lane + 1 ? 1 : 0;
+            }
+            s_tmp2[64 * wave + lane] = mine;
+            __syncthreads();
+            if (c > 0) {
+                int r = s_tmp[128 + c - 1] + s_tmp[64 + c - 1] + below;
+                for (int w = 0; w < wave; ++w)
+                    r += s_tmp2[64 * w + c - 1];
+                s_ord[r] = s;
+            }
+            __syncthreads();
+            if (tid < 64)
+                s_tmp[64 + tid] += s_tmp2[tid] + s_tmp2[64 + tid] + s_tmp2[128 + tid] +
+                                   s_tmp2[192 + tid];
+            __syncthreads();
+        }
+    }
 
-    const int lane = tid & 63, n = lane & 15, kb = lane >> 4;
+    const int n = lane & 15, kb = lane >> 4;
     // Wave-uniform values are made visibly uniform (scalar registers), so
     // that loop bounds, page ids and buffer resources stay scalar.
-    const int total = __builtin_amdgcn_readfirstlane((s_pre[S] + s_pp[S]) * a.slices);
+    const int total = __builtin_amdgcn_readfirstlane((s_pre[S] + s_npart) * a.slices);
     const int nwaves = gridDim.x * kWaves;
     const float sm_log2 = kLog2e / __builtin_sqrtf((float)D);
     const uint8_t* __restrict__ kp = (const uint8_t*)a.k_pool;
@@ -615,7 +671,14 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         }
     };
 
-    int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (tid >> 6));
+    // Wave w takes item w of round 0, then of each round r the item at
+    // w from the round's start (r even) or from its end (r odd).  Item
+    // numbers grow with the round, so a wave's items end at its first round
+    // past the list.
+    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
+    auto item_of = [&](int r) { return r * nwaves + ((r & 1) ? nwaves - 1 - wid : wid); };
+    int round = 0;
+    int item = item_of(0);
     if (item >= total)
         return;
 
@@ -625,10 +688,11 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     // are not computed), so every item starts at ring slot 0.
     // Table entries are fetched two items ahead and held in registers one
     // item ahead, so the ring never waits for them.
-    Item cur = resolve_item<KT, NT, G::CHUNK>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, item);
+    Item cur = resolve_item<KT, NT, G::CHUNK>(s_pre, s_ord, s_len, s_lo, S, Hk, a.slices, item);
     int pid = fetch_pages(a, cur, true);
-    bool has_next = item + nwaves < total;
-    Item nxt = resolve_item<KT, NT, G::CHUNK>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next ? item + nwaves : item);
+    bool has_next = item_of(1) < total;
+    Item nxt = resolve_item<KT, NT, G::CHUNK>(s_pre, s_ord, s_len, s_lo, S, Hk, a.slices,
+                                             has_next ? item_of(1) : item);
     int pid_n = fetch_pages(a, nxt, has_next);
     // A full wait (never too weak): the loop then finds pid and pid_n
     // resolved on entry as it does on every later iteration, and its
@@ -645,9 +709,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
 
     for (;;) {
         // The item after next: geometry and table entries now.
-        const int next2 = item + 2 * nwaves;
+        const int next2 = item_of(round + 2);
         const bool has_next2 = next2 < total;
-        const Item nxt2 = resolve_item<KT, NT, G::CHUNK>(s_pre, s_pp, s_len, s_lo, S, Hk, a.slices, has_next2 ? next2 : item);
+        const Item nxt2 = resolve_item<KT, NT, G::CHUNK>(s_pre, s_ord, s_len, s_lo, S, Hk,
+                                                        a.slices, has_next2 ? next2 : item);
         const int pid_nn = fetch_pages(a, nxt2, has_next2);
 
         const int s = cur.s, j = cur.j, kh = cur.kh, C = cur.C, t0 = cur.t0, t1 = cur.t1;
@@ -749,7 +814,8 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
 
         if (!has_next)
             break;
-        item += nwaves;
+        ++round;
+        item = item_of(round);
         cur = nxt;
         pid = pid_n;
         nxt = nxt2;
