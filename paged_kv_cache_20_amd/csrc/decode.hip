@@ -69,6 +69,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;  // waves per block
 constexpr float kLog2e = 1.4426950408889634f;
@@ -101,6 +102,26 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// The value of lane l ^ 16 (l ^ 32) at lane l, by gfx950's row-pair (half)
+// swap, a VALU operation: no LDS round trip and no counter wait.  Each swap
+// exchanges one operand's odd rows (upper half) with the other's even rows
+// (lower half); with both operands x, lanes of the even rows (lower half)
+// find their partner in the second result, the others in the first.
+__device__ __forceinline__ float xor16_f(float v)
+{
+    const uint32_t x = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const bool odd = (threadIdx.x >> 4) & 1;
+    return __builtin_bit_cast(float, odd ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32_f(float v)
+{
+    const uint32_t x = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const bool upper = (threadIdx.x >> 5) & 1;
+    return __builtin_bit_cast(float, upper ? r[0] : r[1]);
+}
 
 __device__ __forceinline__ int rdlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 __device__ __forceinline__ float rdlane_f(float v, int lane)
@@ -300,8 +321,8 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
                 sv[kblk][r] = in ? x : neg_inf();
                 tmax = fmaxf(tmax, sv[kblk][r]);
             }
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        tmax = fmaxf(tmax, xor16_f(tmax));
+        tmax = fmaxf(tmax, xor32_f(tmax));
         const float mnew = fmaxf(m[tau], tmax);
         const float muse = mnew == neg_inf() ? 0.f : mnew;
         const float al = m[tau] == muse ? 1.f : __builtin_amdgcn_exp2f(m[tau] - muse);
@@ -314,8 +335,8 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
         float psum = (p[0][0] + p[0][1]) + (p[0][2] + p[0][3]);
         if constexpr (KB == 2)
             psum = psum + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-        psum = psum + shfl_xor_f(psum, 16);
-        psum = psum + shfl_xor_f(psum, 32);
+        psum = psum + xor16_f(psum);
+        psum = psum + xor32_f(psum);
         l[tau] = l[tau] * al + psum;
         m[tau] = mnew;
         alpha[tau] = al;
@@ -481,8 +502,12 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     __shared__ int s_ord[kMaxSeq];      // sequences with a partial split, longest first
     __shared__ int s_len[kMaxSeq];
     __shared__ int s_lo[kMaxSeq];  // first key the sequence's first row attends, -1: none
-    __shared__ int s_tmp[256], s_tmp2[256];
-    __shared__ int s_npart;  // partial items
+    // [0, 64): sequences per length class; [64, 128): placed so far; [128,
+    // 192): sequences of longer classes; [192, 196): per-wave item sums.
+    // Class c (1 .. CHUNK/16) is entry c - 1.
+    __shared__ __attribute__((aligned(16))) int s_cls[256];
+    __shared__ int s_cnt[2][256];  // per group of 256 sequences: class counts per wave
+    __shared__ int s_npart;        // partial items
 
     const int S = a.n_seq, R = a.rows, Hk = a.n_head_kv, H = a.n_head;
     const int g = H / Hk, ppt = 16 / g;
@@ -490,8 +515,13 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // The work list, built in LDS by every workgroup alike (item set-up then
-    // waits on no global load).  Lengths, first keys and the exclusive prefix
-    // over sequences of their full items first.
+    // waits on no global load): lengths, first keys, the exclusive prefix
+    // over sequences of their full items, and the order of the partial last
+    // splits -- by length class (pages) from the longest, and by sequence
+    // within a class (a stable counting sort).  With full items first and
+    // each wave taking the items of rounds in alternating directions, the
+    // longest partial items go to the waves with the least work, and the
+    // last items of the grid are the shortest.
     {
         // lo: first key of the sequence's first row; -1 marks a sequence
         // whose floor lies outside 0 .. that row's position (no items, NaN).
@@ -507,6 +537,14 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             const int end = a.below_round ? (C - R) / G::CHUNK : C / G::CHUNK;
             return max(end - lo / G::CHUNK, 0) * Hk;
         };
+        // Length class of a sequence's partial split (0: it has none).
+        auto pclass = [&](int C, int lo) {
+            if (a.below_round || lo < 0 || C % G::CHUNK == 0)
+                return 0;
+            return (C - max(lo, C - C % G::CHUNK) + 15) >> 4;
+        };
+        if (tid < 128)
+            s_cls[tid] = 0;
         const int per = (S + 255) / 256;
         const int b0 = tid * per;
         int loc = 0;
@@ -520,84 +558,75 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
                 loc += nfull(C, lo);
             }
         }
-        s_tmp[tid] = loc;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const int v = tid >= off ? s_tmp[tid - off] : 0;
-            __syncthreads();
-            s_tmp[tid] += v;
-            __syncthreads();
+        int inc = loc;  // inclusive prefix over the wave's threads
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(inc, d, 64);
+            inc += lane >= d ? v : 0;
         }
-        int run = tid ? s_tmp[tid - 1] : 0;
+        if (lane == 63)
+            s_cls[192 + wave] = inc;
+        __syncthreads();
+        int run = inc - loc;
+        for (int w = 0; w < wave; ++w)
+            run += s_cls[192 + w];
         for (int i = 0; i < per; ++i) {
             const int s = b0 + i;
             if (s < S) {
+                const int C = s_len[s], lo = s_lo[s];
                 s_pre[s] = run;
-                run += nfull(s_len[s], s_lo[s]);
+                run += nfull(C, lo);
+                const int c = pclass(C, lo);
+                if (c > 0)
+                    atomicAdd(&s_cls[c - 1], 1);
             }
         }
         if (tid == 255)
-            s_pre[S] = s_tmp[255];
-        __syncthreads();
-    }
-    // Then the order of the partial last splits: by length class (pages,
-    // 1 .. CHUNK/16) from the longest, and by sequence within a class (a
-    // stable counting sort).  With full items first and each wave taking
-    // the items of rounds in alternating directions, the longest partial
-    // items go to the waves with the least work, and the last items of the
-    // grid are the shortest.
-    {
-        // Length class of sequence s's partial split (0: it has none).
-        auto pclass = [&](int s) {
-            const int C = s_len[s], lo = s_lo[s];
-            if (a.below_round || lo < 0 || C % G::CHUNK == 0)
-                return 0;
-            return (C - max(lo, C - C % G::CHUNK) + 15) >> 4;
-        };
-        // s_tmp[0, 64): sequences per class; [64, 128): placed so far;
-        // [128, 192): sequences of longer classes.  Class c is entry c - 1.
-        if (tid < 64)
-            s_tmp[tid] = s_tmp[64 + tid] = 0;
-        __syncthreads();
-        for (int s = tid; s < S; s += 256) {
-            const int c = pclass(s);
-            if (c > 0)
-                atomicAdd(&s_tmp[c - 1], 1);
-        }
+            s_pre[S] = run;  // the last thread's range ends the list
         __syncthreads();
         if (tid < 64) {
             int longer = 0;
-            for (int c = tid + 1; c < 64; ++c)
-                longer += s_tmp[c];
-            s_tmp[128 + tid] = longer;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const i32x4 v = *(const i32x4*)&s_cls[4 * q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    longer += 4 * q + e > tid ? v[e] : 0;
+            }
+            s_cls[128 + tid] = longer;
             if (tid == 0)
-                s_npart = (longer + s_tmp[0]) * Hk;
+                s_npart = (longer + s_cls[0]) * Hk;
         }
         __syncthreads();
-        for (int s0 = 0; s0 < S; s0 += 256) {
+        for (int s0 = 0, par = 0; s0 < S; s0 += 256, par ^= 1) {
             const int s = s0 + tid;
-            const int c = s < S ? pclass(s) : 0;
-            // Lanes below with the same class; lanes of the wave in class lane + 1.
-            int below = 0, mine = 0;
-            for (int j = 0; j < 64; ++j) {
-                const int cj = rdlane(c, j);
-                below += (j < lane && cj == c) ? 1 : 0;
-                mine += cj == lane + 1 ? 1 : 0;
+            const int c = s < S ? pclass(s_len[s], s_lo[s]) : 0;
+            // Lanes of the wave in class c (same) and in class lane + 1 (mine),
+            // from one ballot per bit of the class.
+            uint64_t same = ~0ull, mine = ~0ull;
+#pragma unroll
+            for (int k = 0; k < 7; ++k) {
+                const uint64_t bk = __builtin_amdgcn_ballot_w64(((c >> k) & 1) != 0);
+                same &= ((c >> k) & 1) ? bk : ~bk;
+                mine &= (((lane + 1) >> k) & 1) ? bk : ~bk;
             }
-            s_tmp2[64 * wave + lane] = mine;
+            const int below = (int)__builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
+            s_cnt[par][64 * wave + lane] = __builtin_popcountll(mine);
             __syncthreads();
             if (c > 0) {
-                int r = s_tmp[128 + c - 1] + s_tmp[64 + c - 1] + below;
+                int r = s_cls[128 + c - 1] + s_cls[64 + c - 1] + below;
                 for (int w = 0; w < wave; ++w)
-                    r += s_tmp2[64 * w + c - 1];
+                    r += s_cnt[par][64 * w + c - 1];
                 s_ord[r] = s;
             }
-            __syncthreads();
-            if (tid < 64)
-                s_tmp[64 + tid] += s_tmp2[tid] + s_tmp2[64 + tid] + s_tmp2[128 + tid] +
-                                   s_tmp2[192 + tid];
-            __syncthreads();
+            if (s0 + 256 < S) {
+                __syncthreads();
+                if (tid < 64)
+                    s_cls[64 + tid] += s_cnt[par][tid] + s_cnt[par][64 + tid] +
+                                       s_cnt[par][128 + tid] + s_cnt[par][192 + tid];
+            }
         }
+        __syncthreads();
     }
 
     const int n = lane & 15, kb = lane >> 4;
