@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/pagedattn.h"
 #include "kernels.h"
@@ -27,6 +28,52 @@ thread_local char t_err[256] = "";
 thread_local hipEvent_t t_ev_start = nullptr;
 thread_local hipEvent_t t_ev_stop = nullptr;
 std::atomic<int32_t> g_max_workgroups{0};
+
+// The mixed step's second stream and compute-unit count, per device, made
+// on first use with that device current and kept until the process ends;
+// and each thread's fork / join events per device.
+std::mutex g_side_mu;
+hipStream_t g_side[pa::kMaxDevices];
+int g_cus[pa::kMaxDevices];
+thread_local hipEvent_t t_fork[pa::kMaxDevices];
+thread_local hipEvent_t t_join[pa::kMaxDevices];
+
+hipError_t side_stream(hipStream_t* side, int* cus, hipEvent_t* fork, hipEvent_t* join)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= pa::kMaxDevices)
+        return hipErrorInvalidDevice;
+    {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        if (!g_side[dev]) {
+            int n = 0;
+            e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess)
+                return e;
+            hipStream_t st = nullptr;
+            e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+            if (e != hipSuccess)
+                return e;
+            g_cus[dev] = n;
+            g_side[dev] = st;
+        }
+        *side = g_side[dev];
+        *cus = g_cus[dev];
+    }
+    for (hipEvent_t* ev : {&t_fork[dev], &t_join[dev]}) {
+        if (!*ev) {
+            e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    *fork = t_fork[dev];
+    *join = t_join[dev];
+    return hipSuccess;
+}
 
 int fail(int code, const char* fmt, ...)
 {
@@ -152,7 +199,7 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
                int32_t page_size, attn_kv_dtype kv_dtype, void* out, void* workspace,
                size_t workspace_bytes, hipStream_t stream, int32_t window = 0,
                const int32_t* kv_floor = nullptr, int below_round = 0, int phase = 0,
-               bool noalloc = false)
+               bool noalloc = false, int32_t max_blocks = 0)
 {
     int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                           max_pages, n_head, n_head_kv, head_dim, page_size, kv_dtype, out);
@@ -223,6 +270,8 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     a.ev_stop = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
     a.max_blocks = g_max_workgroups.load(std::memory_order_relaxed);
+    if (max_blocks > 0 && (a.max_blocks == 0 || max_blocks < a.max_blocks))
+        a.max_blocks = max_blocks;
     a.window = window;
     a.kv_floor = kv_floor;
     a.below_round = below_round;
@@ -628,16 +677,39 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
                     fn, n_tok, n_seq);
     }
 
+    // With both halves, the chunk half runs on a second stream beside the
+    // decode half: the decode kernel (bound by HBM) takes three quarters of
+    // the compute units, and the chunk's workgroups (bound by the matrix
+    // units) start on the rest and fill in beside it.  The chunk then uses
+    // four-wave workgroups, which fit on a CU next to a decode workgroup.
+    // Which CU runs a row changes none of its arithmetic.
+    const bool both = n_seq_decode > 0 && n_chunk > 0;
+    hipStream_t side = stream;
+    hipEvent_t fork = nullptr, join = nullptr;
+    int cus = 0;
+    if (both) {
+        rc = from_hip(side_stream(&side, &cus, &fork, &join), fn);
+        if (rc != ATTN_OK)
+            return rc;
+    }
     hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
     if (ev0)
         (void)hipEventRecord(ev0, stream);
+    if (both) {
+        rc = from_hip(hipEventRecord(fork, stream), fn);
+        if (rc == ATTN_OK)
+            rc = from_hip(hipStreamWaitEvent(side, fork, 0), fn);
+        if (rc != ATTN_OK)
+            return rc;
+    }
     // Decode half: sequences 0 .. n_seq_decode - 1, one row each, at token
     // rows 0 .. n_seq_decode - 1 (the step is ordered decode-first).
     if (n_seq_decode > 0) {
         rc = split_call(fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                         max_pages_per_seq, ctx_lens, n_seq_decode, n_head, n_head_kv, head_dim,
-                        page_size, kv_dtype, out, workspace, workspace_bytes, stream);
+                        page_size, kv_dtype, out, workspace, workspace_bytes, stream, 0, nullptr,
+                        0, 0, false, both ? cus * 3 / 4 : 0);
         if (rc != ATTN_OK)
             return rc;
     }
@@ -668,7 +740,15 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
         a.n_tok = n_tok;
         a.window = 0;
         a.kv_floor = 0;
-        rc = from_hip(pa::launch_prefill(a, stream), fn);
+        a.narrow = both ? 1 : 0;
+        rc = from_hip(pa::launch_prefill(a, side), fn);
+        if (rc != ATTN_OK)
+            return rc;
+    }
+    if (both) {
+        rc = from_hip(hipEventRecord(join, side), fn);
+        if (rc == ATTN_OK)
+            rc = from_hip(hipStreamWaitEvent(stream, join, 0), fn);
         if (rc != ATTN_OK)
             return rc;
     }

@@ -117,6 +117,10 @@ struct PrefillArgs {
     // fp8 cache only: QK^T on the fp8 matrix unit, K with its stored codes,
     // each query vector rounded to E4M3 at a power-of-two scale.
     int qk_fp8 = 0;
+    // fp8 cache at head_dim 128: workgroups of four waves (64 query rows),
+    // which leave a CU room for a decode workgroup beside them.  A row's
+    // arithmetic is the same as with eight.
+    int narrow = 0;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // The bf16-cache prefill with score and output waves (prefill_pipe.hip);

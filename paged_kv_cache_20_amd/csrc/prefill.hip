@@ -280,7 +280,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w)
 }
 
 template <int D, bool FP8, int RT, int NW, bool QF8>
-__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(PrefillArgs a)
+__global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
 {
     using G = PGeo<D, FP8, RT, NW>;
     static_assert(!QF8 || (FP8 && RT == 1), "fp8 QK^T: fp8 cache, one row tile per wave");
@@ -572,46 +572,42 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         rawv = rawk;
         rawk = fetch_page(b, tile0 + 3 * kKT + wk);
 
-        // Scale (log2 units) and, on a tile that crosses the causal edge or
-        // the first key of some row, mask; then the lane-local max check.
+        // On a tile that crosses the causal edge or the first key of some
+        // row, mask (-inf); then each lane's max of its scaled scores.  The
+        // scale is applied inside the exponent below either way, so whether
+        // the workgroup counts a tile as crossing changes no row's bits.
         const bool diag = tile0 + kKT - 1 > minpos || tile0 < lo_max;
         float sx[4];  // factor applied to cur in the exponent
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq)
             sx[kq] = FP8 ? kc[kq] * smq : sm_log2;
-        float lmax[RT];
         if (diag) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float mx = neg_inf();
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int key = tile0 + 16 * kq + 4 * kb + x;
-                        const float v = key > pos[rt] || key < klo[rt] ? neg_inf()
-                                                                        : cur[rt][kq][x] * sx[kq];
-                        cur[rt][kq][x] = v;
-                        mx = fmaxf(mx, v);
+                        if (key > pos[rt] || key < klo[rt])
+                            cur[rt][kq][x] = neg_inf();
                     }
-                lmax[rt] = mx;
-            }
-#pragma unroll
-            for (int kq = 0; kq < 4; ++kq)
-                sx[kq] = 1.f;
-        } else {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float mx = neg_inf();
-#pragma unroll
-                for (int kq = 0; kq < 4; ++kq) {
-                    const float bm = fmaxf(fmaxf(cur[rt][kq][0], cur[rt][kq][1]),
-                                           fmaxf(cur[rt][kq][2], cur[rt][kq][3]));
-                    mx = FP8 ? fmaxf(mx, bm * sx[kq]) : fmaxf(mx, bm);
-                }
-                lmax[rt] = FP8 ? mx : mx * sm_log2;
-            }
         }
+        float lmax[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float mx = neg_inf();
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                const float bm = fmaxf(fmaxf(cur[rt][kq][0], cur[rt][kq][1]),
+                                       fmaxf(cur[rt][kq][2], cur[rt][kq][3]));
+                mx = FP8 ? fmaxf(mx, bm * sx[kq]) : fmaxf(mx, bm);
+            }
+            lmax[rt] = FP8 ? mx : mx * sm_log2;
+        }
+        // Lazy rescale, decided per row: a row moves its max only when a
+        // tile's max passes it by more than kTau, so a row's arithmetic never
+        // depends on the other rows of its wave (or on the workgroup's size).
         bool up = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -619,14 +615,15 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
         if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const float mnew = fmaxf(m[rt], row_max4(lmax[rt]));
+                const float rm = row_max4(lmax[rt]);
+                const bool need = rm > m[rt] + kTau;
                 const float alpha =
-                    m[rt] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mnew);
+                    !need ? 1.f : m[rt] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(m[rt] - rm);
                 l[rt] = l[rt] * alpha;
 #pragma unroll
                 for (int jb = 0; jb < G::DBLK; ++jb)
                     O[rt][jb] = O[rt][jb] * alpha;
-                m[rt] = mnew;
+                m[rt] = need ? rm : m[rt];
             }
         }
 
@@ -647,8 +644,10 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 2 : 1)) void prefill_kernel(Pre
                 float pe[4];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    pe[x] =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(cur[rt][kq][x], sx[kq], -muse[rt]));
+                    // (a masked key stays -inf whatever the page scale, 0 included)
+                    const float c = cur[rt][kq][x];
+                    pe[x] = __builtin_amdgcn_exp2f(
+                        c == neg_inf() ? neg_inf() : __builtin_fmaf(c, sx[kq], -muse[rt]));
                     e[rt][kq][x] = FP8 ? pe[x] * vsc : pe[x];
                 }
                 l[rt] = l[rt] + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
@@ -775,6 +774,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
             return launch_t<256, true, 1, 8, true>(a, stream);
         return hipErrorNotSupported;
     }
+    if (a.narrow && a.fp8 && a.head_dim == 128)
+        return launch_t<128, true, 1, 4>(a, stream);
     if (!a.fp8) {
         const hipError_t e = launch_prefill_pipe(a, stream);
         if (e != hipErrorNotSupported)

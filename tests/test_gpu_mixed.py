@@ -62,6 +62,9 @@ STEPS = [
     ("mx_bf16_g4", [700, 33, 1025, 512, 90], [(300, 300), (1000, 77), (513, 64)], 8, 2, 128,
      False),
     ("mx_fp8_d256", [2000, 17], [(1500, 130)], 16, 4, 256, True),
+    # fp8 at head_dim 128: the chunk half in four-wave workgroups beside the decode
+    ("mx_fp8_d128", [3000, 17, 1024, 700], [(2048, 200), (600, 64), (90, 90)], 32, 8, 128,
+     True),
     ("mx_g8_chunks_only", [], [(40, 40), (900, 129)], 32, 4, 128, False),
     ("mx_decode_only", [100, 5000, 640], [], 8, 2, 128, False),
 ]
