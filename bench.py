@@ -170,18 +170,29 @@ class Bench:
         torch.cuda.synchronize()
         return st
 
-    def split_step(self, st, timer=None):
+    def split_step(self, st, timer=None, marks=None):
+        """One step: the append (A0) of every sequence's new rows, then the
+        attention call.  `timer`: HIP events around the split kernel;
+        `marks`: three torch events recorded before the append, between the
+        two calls and after the attention call (the library launches on
+        torch's current stream)."""
         pa = self.pa
         w, inp = st["w"], st["inp"]
+        if marks is not None:
+            marks[0].record()
         pa.attn_kv_append(st["k_new"], st["v_new"], st["slots_new"], st["slots_new"].numel(),
                           st["k"], st["v"], st["ks"], st["vs"], inp.n_pages, w.n_head_kv,
                           w.head_dim, 16, st["kv"])
+        if marks is not None:
+            marks[1].record()
         if timer is not None:
             pa.attn_set_kernel_timer(timer[0], timer[1])
         fn = pa.attn_paged_decode if w.kind == "decode" else pa.attn_paged_verify
         fn(inp.q, st["k"], st["v"], st["ks"], st["vs"], inp.n_pages, inp.table, w.max_pages,
            inp.lengths, w.n_seq, w.n_head, w.n_head_kv, w.head_dim, 16, st["kv"], st["out"],
            st["ws"], st["wsb"])
+        if marks is not None:
+            marks[2].record()
 
     def time_split(self, st, steps, warmup):
         torch = self.torch
@@ -189,16 +200,21 @@ class Bench:
             self.split_step(st)
         torch.cuda.synchronize()
         evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
+        marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.split_step(st, evs[i])
+            self.split_step(st, evs[i], marks[i])
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
         kern = [self.ev.elapsed_ms(a, b) for a, b in evs]
         for a, b in evs:
             self.ev.destroy(a)
             self.ev.destroy(b)
+        app = sorted(m[0].elapsed_time(m[1]) for m in marks)
+        call = sorted(m[1].elapsed_time(m[2]) for m in marks)
+        st["append_us_median"] = round(app[len(app) // 2] * 1e3, 2)
+        st["call_us_median"] = round(call[len(call) // 2] * 1e3, 2)
         return wall, sum(kern) / len(kern), sorted(kern)[len(kern) // 2]
 
     def setup_prefill(self, name, w=None):
@@ -554,7 +570,8 @@ def main():
     log("[bench] headline", name)
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-              "dtype": "bf16", "data": "synthetic"}
+              "dtype": "fp8-e4m3 KV, bf16 MFMA, fp32 accumulation" if w.kv_fp8 else "bf16",
+              "data": "synthetic"}
     if w.kind == "prefill":
         st = b.setup_prefill(name)
         wall, kavg, kmed = b.time_prefill(st, args.steps, args.warmup)
@@ -584,6 +601,11 @@ def main():
                               "kernel": "split_kernel", "kernel_avg_us": round(kavg * 1e3, 2),
                               "kernel_median_us": round(kmed * 1e3, 2),
                               "algorithmic_bytes_per_launch": split_bytes}
+        # The step's parts by events on the stream: the append (A0) of the
+        # step's new rows, and the attention call (split + combine kernels).
+        result["append_us_median"] = st["append_us_median"]
+        result["attention_call_us_median"] = st["call_us_median"]
+        result["append_bytes"] = append_bytes(w.n_seq * w.rows, w)
     result["config"] = {"workload": name, "n_seq": w.n_seq, "rows": w.rows, "n_head": w.n_head,
                         "n_head_kv": w.n_head_kv, "head_dim": w.head_dim, "page_size": 16,
                         "kv_dtype": "fp8-e4m3" if w.kv_fp8 else "bf16",

@@ -80,9 +80,9 @@
  * Determinism: decode and verify results depend only on the sequence's own
  * inputs -- never on the batch size, the other sequences, the order of the
  * batch or the device's compute-unit count -- and each verify row is bit for
- * bit the decode result for the same position over the same cache
- * ("TandemLLM -- Adding a model", section "The adapter path in ten steps",
- * step 4: every verified row must equal the decode step's row bit for bit).
+ * bit the decode result for the same position over the same cache, as the
+ * pages ask of a speculative round ("TandemLLM -- Adding a model", section
+ * "The adapter path in ten steps", step 4).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -396,12 +396,17 @@ int attn_paged_prefill_window(const void* q, int32_t n_rows, const void* k_pool,
  *   slot_mapping  int32 [n_tok]
  * bf16 pools: a copy.  fp8 pools: a page's K scale and V scale are set to
  * absmax / 448 (1 when absmax is 0) over this call's rows in that page, by
- * the call that writes the page's offset 0; a call that writes only later
- * offsets keeps the stored scale.  Each code is the E4M3 value nearest to
- * the fp32 quotient x / scale, ties to even, saturating at +-448.
+ * the call that writes the page's offset 0.  A call that writes only later
+ * offsets keeps the stored scale s while its rows fit (fp32 absmax / s <=
+ * 448); otherwise the scale doubles until they do, and the codes already in
+ * the page's slots below the call's first one are re-encoded at the new
+ * scale s' (nearest E4M3 to fp32(fp32(value * s) / s'), exact for codes that
+ * stay normal), so a page filled one token per call keeps E4M3's precision.
+ * Each new code is the E4M3 value nearest to the fp32 quotient x / scale,
+ * ties to even, saturating at +-448.
  * Precondition for fp8: the rows a call writes into one page are adjacent
  * in the call, in increasing offset order (true of any sequence's run of
- * new tokens).  Slots must lie below n_pages * page_size; a larger slot
+ * new tokens); two runs of one page in one call race on its scale.  Slots must lie below n_pages * page_size; a larger slot
  * skips its row.
  */
 int attn_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,

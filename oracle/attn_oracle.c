@@ -363,10 +363,16 @@ int oracle_round_q_e4m3(const uint16_t *q, int64_t n_vec, int32_t head_dim, uint
  * fp8: one fp32 scale per (page, kv head), separately for K and for V, equal
  * to absmax / 448 ("one fp32 scale per page per KV head (absmax/448)"), where
  * absmax runs over every element of this call's rows that land in that page
- * and head.  A page's scale is (re)set only by a call that writes the page's
- * first slot (offset 0); a call that writes later slots of a page keeps the
- * scale already stored and saturates.  A zero absmax gives scale 1.  Each
- * element's code is the nearest E4M3 value to the fp32 quotient x / scale.
+ * and head.  A call that writes the page's first slot (offset 0) sets the
+ * scale from its own rows (a zero absmax gives scale 1).  A call that writes
+ * only later slots keeps the stored scale s while its rows fit (fp32 absmax
+ * / s <= 448); otherwise the scale doubles until they fit (s' = s * 2^k,
+ * the least k >= 1 with fp32 absmax / s' <= 448; a non-finite absmax never
+ * grows it) and the codes already in the page's slots below the call's first
+ * one are re-encoded at s': code' = nearest E4M3 to fp32(fp32(value(code) *
+ * s) / s'), which is exact for every code that stays a normal number.  Each
+ * new element's code is the nearest E4M3 value to the fp32 quotient x /
+ * scale.
  *
  * Returns 0, or -1 for a slot outside the pool.
  */
@@ -397,22 +403,28 @@ int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new,
         }
         return 0;
     }
-    /* fp8: first the scales of pages whose first slot this call writes:
-       mark those pages, take absmax over every row of the call that lands in
-       a marked page, then store absmax / 448 (1 for a zero absmax). */
+    /* fp8: first the scales of the pages this call writes: the first slot
+       each page receives (page_size if none), absmax over every row of the
+       call that lands in the page, then a new scale from offset 0, or a grown
+       scale (with the earlier slots' codes re-encoded), or the stored one. */
     {
-        uint8_t *reset = (uint8_t *)calloc((size_t)n_pages, 1);
+        int *first = (int *)malloc(sizeof(int) * (size_t)n_pages);
         float *amax = (float *)calloc((size_t)(n_pages * n_head_kv), sizeof(float));
-        for (int t = 0; t < n_tok; ++t)
-            if (slot_mapping[t] >= 0 && slot_mapping[t] % page_size == 0)
-                reset[slot_mapping[t] / page_size] = 1;
+        for (int64_t page = 0; page < n_pages; ++page)
+            first[page] = page_size;
+        for (int t = 0; t < n_tok; ++t) {
+            int64_t slot = slot_mapping[t];
+            if (slot >= 0 && slot % page_size < first[slot / page_size])
+                first[slot / page_size] = (int)(slot % page_size);
+        }
         for (int kv = 0; kv < 2; ++kv) {
             const uint16_t *src = kv ? v_new : k_new;
             float *scale = kv ? v_scale : k_scale;
+            uint8_t *pool = (uint8_t *)(kv ? v_pool : k_pool);
             memset(amax, 0, sizeof(float) * (size_t)(n_pages * n_head_kv));
             for (int t = 0; t < n_tok; ++t) {
                 int64_t slot = slot_mapping[t];
-                if (slot < 0 || !reset[slot / page_size])
+                if (slot < 0)
                     continue;
                 int64_t page = slot / page_size;
                 for (int h = 0; h < n_head_kv; ++h)
@@ -422,14 +434,31 @@ int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new,
                             amax[page * n_head_kv + h] = x;
                     }
             }
-            for (int64_t page = 0; page < n_pages; ++page)
-                if (reset[page])
-                    for (int h = 0; h < n_head_kv; ++h) {
-                        float a = amax[page * n_head_kv + h];
-                        scale[page * n_head_kv + h] = a > 0.0f ? a / 448.0f : 1.0f;
+            for (int64_t page = 0; page < n_pages; ++page) {
+                if (first[page] == page_size)
+                    continue; /* not written by this call */
+                for (int h = 0; h < n_head_kv; ++h) {
+                    float a = amax[page * n_head_kv + h];
+                    float *sc = &scale[page * n_head_kv + h];
+                    if (first[page] == 0) {
+                        *sc = a > 0.0f ? a / 448.0f : 1.0f;
+                    } else if (a <= 3.4028234663852886e38f && a / *sc > 448.0f) {
+                        float s_old = *sc, s_new = s_old;
+                        while (a / s_new > 448.0f)
+                            s_new = s_new * 2.0f;
+                        for (int off = 0; off < first[page]; ++off)
+                            for (int i = 0; i < head_dim; ++i) {
+                                uint8_t *c =
+                                    &pool[((page * n_head_kv + h) * page_size + off) * head_dim + i];
+                                float y = (float)oracle_e4m3_value(*c) * s_old;
+                                *c = oracle_e4m3_encode(y / s_new);
+                            }
+                        *sc = s_new;
                     }
+                }
+            }
         }
-        free(reset);
+        free(first);
         free(amax);
     }
     /* then every row's codes, with its page's scale. */

@@ -9,6 +9,7 @@
 // section "Probe: what the plugin measured").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -192,14 +193,15 @@ size_t tree_ws_bytes(int32_t n_seq, int32_t max_pages, int32_t n_head, int32_t h
 }
 
 
-int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
-               const void* v_pool, const float* k_scale, const float* v_scale, int64_t n_pages,
-               const int32_t* block_table, int32_t max_pages, const int32_t* ctx_lens,
-               int32_t n_seq, int32_t n_head, int32_t n_head_kv, int32_t head_dim,
-               int32_t page_size, attn_kv_dtype kv_dtype, void* out, void* workspace,
-               size_t workspace_bytes, hipStream_t stream, int32_t window = 0,
-               const int32_t* kv_floor = nullptr, int below_round = 0, int phase = 0,
-               bool noalloc = false, int32_t max_blocks = 0)
+// Host checks of a decode / verify call and its kernel arguments; enqueues
+// nothing.
+int split_setup(pa::SplitArgs& a, const char* fn, int32_t rows, const void* q,
+                const void* k_pool, const void* v_pool, const float* k_scale,
+                const float* v_scale, int64_t n_pages, const int32_t* block_table,
+                int32_t max_pages, const int32_t* ctx_lens, int32_t n_seq, int32_t n_head,
+                int32_t n_head_kv, int32_t head_dim, int32_t page_size, attn_kv_dtype kv_dtype,
+                void* out, void* workspace, size_t workspace_bytes, int32_t window,
+                const int32_t* kv_floor, int below_round, int phase, bool noalloc)
 {
     int rc = check_common(fn, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
                           max_pages, n_head, n_head_kv, head_dim, page_size, kv_dtype, out);
@@ -214,11 +216,6 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     const int g = n_head / n_head_kv;
     if (g > 16)
         return fail(ATTN_E_UNSUPPORTED, "%s: %d query heads per kv head (at most 16)", fn, g);
-    const int nt = pa::split_tiles(rows, g);
-    if (nt * head_dim > 512)
-        return fail(ATTN_E_UNSUPPORTED,
-                    "%s: %d rows x %d heads per kv head at head_dim %d not served", fn, rows, g,
-                    head_dim);
     // One sequence's query rows, and one split's partial outputs, are each
     // addressed through a buffer resource spanning less than 2 GiB.
     if ((int64_t)rows * n_head * head_dim * 4 >= ((int64_t)1 << 31))
@@ -244,7 +241,6 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     if (rc != ATTN_OK)
         return rc;
 
-    pa::SplitArgs a;
     a.q = q;
     a.k_pool = k_pool;
     a.v_pool = v_pool;
@@ -270,16 +266,45 @@ int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
     a.ev_stop = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
     a.max_blocks = g_max_workgroups.load(std::memory_order_relaxed);
-    if (max_blocks > 0 && (a.max_blocks == 0 || max_blocks < a.max_blocks))
-        a.max_blocks = max_blocks;
     a.window = window;
     a.kv_floor = kv_floor;
     a.below_round = below_round;
     a.phase = phase;
+    return ATTN_OK;
+}
+
+int split_call(const char* fn, int32_t rows, const void* q, const void* k_pool,
+               const void* v_pool, const float* k_scale, const float* v_scale, int64_t n_pages,
+               const int32_t* block_table, int32_t max_pages, const int32_t* ctx_lens,
+               int32_t n_seq, int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+               int32_t page_size, attn_kv_dtype kv_dtype, void* out, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, int32_t window = 0,
+               const int32_t* kv_floor = nullptr, int below_round = 0, int phase = 0,
+               bool noalloc = false)
+{
+    pa::SplitArgs a;
+    const int rc = split_setup(a, fn, rows, q, k_pool, v_pool, k_scale, v_scale, n_pages,
+                               block_table, max_pages, ctx_lens, n_seq, n_head, n_head_kv,
+                               head_dim, page_size, kv_dtype, out, workspace, workspace_bytes,
+                               window, kv_floor, below_round, phase, noalloc);
+    if (rc != ATTN_OK)
+        return rc;
     return from_hip(pa::launch_split_decode(a, stream), fn);
 }
 
 }  // namespace
+
+namespace pa {
+int set_error(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(t_err, sizeof t_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+int clear_error() { return ok(); }
+}  // namespace pa
 
 extern "C" {
 
@@ -542,10 +567,8 @@ int attn_paged_verify_tree(const void* q, void* k_pool, void* v_pool, float* k_s
     // every view over all its splits (one launch, the same bits).
     void* ws = (char*)workspace + off_split;
     const size_t wsb = workspace_bytes - off_split;
-    const int g = n_head / n_head_kv;
     const int64_t ms = pa::max_splits(max_pages_per_seq, ATTN_PAGE_SIZE);
     const bool shared =
-        pa::split_tiles(width, g) * head_dim <= 512 &&
         ((int64_t)(width - 1) * ms * n_head + n_head) * head_dim * 4 < ((int64_t)1 << 31);
     rc = from_hip(pa::launch_tree_stage(t, stream), fn);
     if (rc != ATTN_OK)
@@ -684,16 +707,29 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
     // four-wave workgroups, which fit on a CU next to a decode workgroup.
     // Which CU runs a row changes none of its arithmetic.
     const bool both = n_seq_decode > 0 && n_chunk > 0;
-    hipStream_t side = stream;
-    hipEvent_t fork = nullptr, join = nullptr;
-    int cus = 0;
-    if (both) {
-        rc = from_hip(side_stream(&side, &cus, &fork, &join), fn);
+    hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    // Decode half: sequences 0 .. n_seq_decode - 1, one row each, at token
+    // rows 0 .. n_seq_decode - 1 (the step is ordered decode-first); checked
+    // before anything is enqueued.
+    pa::SplitArgs da;
+    if (n_seq_decode > 0) {
+        rc = split_setup(da, fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
+                         max_pages_per_seq, ctx_lens, n_seq_decode, n_head, n_head_kv, head_dim,
+                         page_size, kv_dtype, out, workspace, workspace_bytes, 0, nullptr, 0, 0,
+                         false);
         if (rc != ATTN_OK)
             return rc;
     }
-    hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
-    t_ev_start = t_ev_stop = nullptr;
+    hipStream_t side = stream;
+    hipEvent_t fork = nullptr, join = nullptr;
+    if (both) {
+        int cus = 0;
+        rc = from_hip(side_stream(&side, &cus, &fork, &join), fn);
+        if (rc != ATTN_OK)
+            return rc;
+        da.max_blocks = da.max_blocks > 0 ? std::min(da.max_blocks, cus * 3 / 4) : cus * 3 / 4;
+    }
     if (ev0)
         (void)hipEventRecord(ev0, stream);
     if (both) {
@@ -703,13 +739,8 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
         if (rc != ATTN_OK)
             return rc;
     }
-    // Decode half: sequences 0 .. n_seq_decode - 1, one row each, at token
-    // rows 0 .. n_seq_decode - 1 (the step is ordered decode-first).
     if (n_seq_decode > 0) {
-        rc = split_call(fn, 1, q, k_pool, v_pool, k_scale, v_scale, n_pages, block_table,
-                        max_pages_per_seq, ctx_lens, n_seq_decode, n_head, n_head_kv, head_dim,
-                        page_size, kv_dtype, out, workspace, workspace_bytes, stream, 0, nullptr,
-                        0, 0, false, both ? cus * 3 / 4 : 0);
+        rc = from_hip(pa::launch_split_decode(da, stream), fn);
         if (rc != ATTN_OK)
             return rc;
     }

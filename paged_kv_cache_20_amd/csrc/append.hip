@@ -6,8 +6,15 @@
 // fp8: one scale per (page, kv head), separately for K and V, set to
 // absmax / 448 by the call that writes the page's offset 0, over that call's
 // rows in the page (the "one fp32 scale per page per KV head (absmax/448)"
-// layout); later calls reuse the stored scale.  A code is the OCP E4M3 value
+// layout).  A later call keeps the stored scale while its rows fit (fp32
+// absmax / scale <= 448); otherwise it doubles the scale until they fit and
+// re-encodes the codes already in the page's earlier slots at the new scale
+// (exact for every code that stays a normal number), so rows appended one
+// token at a time keep E4M3's precision.  A code is the OCP E4M3 value
 // nearest to x / scale (fp32 quotient), ties to even, saturating at 448.
+// The rows a call writes into one page must be one run of consecutive rows
+// at consecutive offsets: runs of one page are not ordered against each
+// other.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +46,17 @@ __device__ __forceinline__ uint32_t e4m3_code(float y)
     return sign | (r - (120u << 3));
 }
 
+// Value of an E4M3 code (exact in fp32); NaN for the two NaN codes.
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    if ((c & 0x7Fu) == 0x7Fu)
+        return __builtin_nanf("");
+    const float v = e == 0 ? (float)m * 0.001953125f  // m * 2^-9
+                           : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+
 // bf16: one thread per 16-byte piece of a K (and the same V) row.
 template <int D>
 __global__ __launch_bounds__(256) void append_bf16(AppendArgs a)
@@ -63,7 +81,8 @@ __global__ __launch_bounds__(256) void append_bf16(AppendArgs a)
 
 // fp8: one wave per (row, kv head) that starts a run of rows landing in one
 // page at consecutive offsets; the wave sets the scales (if the run starts at
-// offset 0) and writes the run's codes.
+// offset 0), grows them (re-encoding the page's earlier codes) if the run
+// does not fit, and writes the run's codes.
 template <int D>
 __global__ __launch_bounds__(256) void append_fp8(AppendArgs a)
 {
@@ -94,23 +113,39 @@ __global__ __launch_bounds__(256) void append_fp8(AppendArgs a)
         const uint16_t* src = (const uint16_t*)(kv ? a.v_new : a.k_new);
         uint8_t* pool = (uint8_t*)(kv ? a.v_pool : a.k_pool);
         float* scales = kv ? a.v_scale : a.k_scale;
+        float amax = 0.f;
+        for (int u = 0; u < len; ++u) {
+            const uint16_t* row = src + ((int64_t)(t + u) * Hk + h) * D;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(row[lane + 64 * e])));
+        }
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1)
+            amax = __builtin_fmaxf(amax, __shfl_xor(amax, msk, 64));
         float scale;
         if (off == 0) {
-            float amax = 0.f;
-            for (int u = 0; u < len; ++u) {
-                const uint16_t* row = src + ((int64_t)(t + u) * Hk + h) * D;
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_to_f32(row[lane + 64 * e])));
-            }
-#pragma unroll
-            for (int msk = 32; msk >= 1; msk >>= 1)
-                amax = __builtin_fmaxf(amax, __shfl_xor(amax, msk, 64));
             scale = amax > 0.f ? amax / 448.f : 1.f;
             if (lane == 0)
                 scales[sc_idx] = scale;
         } else {
             scale = scales[sc_idx];
+            if (amax <= 3.4028234663852886e38f && amax / scale > 448.f) {
+                float ns = scale;
+                while (amax / ns > 448.f)
+                    ns = ns * 2.f;
+                for (int u = 0; u < off; ++u) {
+                    uint8_t* row = pool + ((page * Hk + h) * 16 + u) * D;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float y = e4m3_value(row[lane + 64 * e]) * scale;
+                        row[lane + 64 * e] = (uint8_t)e4m3_code(y / ns);
+                    }
+                }
+                scale = ns;
+                if (lane == 0)
+                    scales[sc_idx] = ns;
+            }
         }
         for (int u = 0; u < len; ++u) {
             const uint16_t* row = src + ((int64_t)(t + u) * Hk + h) * D;

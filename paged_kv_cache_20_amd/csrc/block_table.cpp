@@ -11,6 +11,13 @@
 
 #include "../../include/pagedattn.h"
 
+namespace pa {
+// Sets the calling thread's attn_last_error() message; returns `code`
+// (api.cpp).
+int set_error(int code, const char* fmt, ...);
+int clear_error();
+}  // namespace pa
+
 namespace {
 
 struct SplitMix64 {
@@ -31,22 +38,31 @@ extern "C" int attn_block_table_build(int32_t n_seq, const int32_t* ctx_lens_hos
                                       int32_t max_pages_per_seq, int32_t* block_table_host,
                                       int32_t* slot_mapping_host)
 {
-    if (!ctx_lens_host || !block_table_host || n_seq <= 0 || page_size <= 0 ||
-        pool_pages <= 0 || max_pages_per_seq <= 0 || pool_pages > (int64_t)INT32_MAX) {
-        // The error string lives in api.cpp; keep this helper self-contained.
-        return ATTN_E_ARG;
-    }
+    const char* fn = "attn_block_table_build";
+    if (!ctx_lens_host || !block_table_host)
+        return pa::set_error(ATTN_E_ARG, "%s: ctx_lens_host/block_table_host is NULL", fn);
+    if (n_seq <= 0 || page_size <= 0 || max_pages_per_seq <= 0)
+        return pa::set_error(ATTN_E_ARG,
+                             "%s: n_seq %d, page_size %d and max_pages_per_seq %d must be positive",
+                             fn, n_seq, page_size, max_pages_per_seq);
+    if (pool_pages <= 0 || pool_pages > (int64_t)INT32_MAX)
+        return pa::set_error(ATTN_E_ARG, "%s: pool_pages %lld outside 1 .. 2^31 - 1", fn,
+                             (long long)pool_pages);
     int64_t total = 0;
     for (int32_t s = 0; s < n_seq; ++s) {
         if (ctx_lens_host[s] < 0)
-            return ATTN_E_RANGE;
+            return pa::set_error(ATTN_E_RANGE, "%s: ctx_lens_host[%d] = %d is negative", fn, s,
+                                 ctx_lens_host[s]);
         const int64_t need = ((int64_t)ctx_lens_host[s] + page_size - 1) / page_size;
         if (need > max_pages_per_seq)
-            return ATTN_E_RANGE;
+            return pa::set_error(ATTN_E_RANGE,
+                                 "%s: sequence %d needs %lld pages, rows hold %d", fn, s,
+                                 (long long)need, max_pages_per_seq);
         total += need;
     }
     if (total > pool_pages)
-        return ATTN_E_RANGE;
+        return pa::set_error(ATTN_E_RANGE, "%s: the sequences need %lld pages, the pool has %lld",
+                             fn, (long long)total, (long long)pool_pages);
 
     std::vector<int32_t> perm((size_t)pool_pages);
     for (int64_t i = 0; i < pool_pages; ++i)
@@ -71,5 +87,5 @@ extern "C" int attn_block_table_build(int32_t n_seq, const int32_t* ctx_lens_hos
                     (int32_t)((int64_t)row[t / page_size] * page_size + t % page_size);
         }
     }
-    return ATTN_OK;
+    return pa::clear_error();
 }

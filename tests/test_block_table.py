@@ -45,6 +45,10 @@ def test_builder_errors(pa):
     with pytest.raises(pa.AttnError) as e:
         pa.attn_block_table_build([100], 16, 3, 0, 8)  # pool too small
     assert e.value.code == pa.ATTN_E_RANGE
+    assert "pool has 3" in pa.attn_last_error()
     with pytest.raises(pa.AttnError) as e:
         pa.attn_block_table_build([100], 16, 30, 0, 2)  # row too short
     assert e.value.code == pa.ATTN_E_RANGE
+    assert "needs 7 pages" in pa.attn_last_error()
+    pa.attn_block_table_build([100], 16, 30, 0, 8)
+    assert pa.attn_last_error() == ""

@@ -106,12 +106,12 @@ def test_verify_width_host_checks(pa, width, code, needle):
 
 
 def test_verify_width_rejects_unserved_group(pa):
-    # width 5 with 4 heads per kv head at head_dim 256: 2 tiles x 256 fits,
-    # 16 heads per kv head: 5 tiles -> 8 x 256 does not
+    # 32 query heads per kv head: more than one 16-slot tile per position
     with pytest.raises(pa.AttnError) as e:
-        pa.attn_paged_verify_width(**decode_args(width=5, n_head=32, n_head_kv=2,
+        pa.attn_paged_verify_width(**decode_args(width=5, n_head=32, n_head_kv=1,
                                                  head_dim=256))
     assert e.value.code == pa.ATTN_E_UNSUPPORTED
+    assert "at most 16" in str(e.value)
 
 
 def tree_args(**over):
@@ -189,10 +189,11 @@ def test_check_device_host_checks(pa, over, code, needle):
 
 
 def test_verify_rejects_unserved_group(pa):
-    # 16 heads per kv head at head_dim 256: 8 tiles x 256 > 512 accumulator columns
+    # 32 query heads per kv head: more than one 16-slot tile per position
     with pytest.raises(pa.AttnError) as e:
-        pa.attn_paged_verify(**decode_args(n_head=32, n_head_kv=2, head_dim=256))
+        pa.attn_paged_verify(**decode_args(n_head=32, n_head_kv=1, head_dim=256))
     assert e.value.code == pa.ATTN_E_UNSUPPORTED
+    assert "at most 16" in str(e.value)
 
 
 def prefill_args(**over):

@@ -37,6 +37,10 @@ SMALL = [
     L("ver_bf16_d128_g8", [100, 1030], 8, 16, 2, 128, False, 23, kind="verify"),
     L("ver_bf16_d128_g1", [600], 8, 2, 2, 128, False, 24, kind="verify"),
     L("ver_fp8_d256_g2", [17, 1111], 8, 4, 2, 256, True, 25, kind="verify"),
+    # four and eight slot tiles per call: sibling items at head_dim 256 / 128
+    L("ver_bf16_d256_g8", [600, 1030], 8, 16, 2, 256, False, 26, kind="verify"),
+    L("ver_bf16_d128_g16", [300, 1500], 8, 16, 1, 128, False, 27, kind="verify"),
+    L("ver_fp8_d128_g16", [90, 2100], 8, 16, 1, 128, True, 28, kind="verify"),
 ]
 
 

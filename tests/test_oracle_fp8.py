@@ -120,24 +120,73 @@ def test_append_fp8_scale_and_codes(orc):
         assert np.isnan(sc[untouched]).all() and (pool[untouched] == 0x7F).all()
 
 
-def test_append_fp8_later_call_keeps_scale_and_saturates(orc):
+def test_append_fp8_later_call_keeps_or_doubles_scale(orc):
     rng = np.random.default_rng(6)
     Hk, d = 1, 16
     kp, vp, ks, vs = _pools(2, Hk, d, True)
     k1 = bf16_round(rng.standard_normal((5, Hk, d)))
     orc.kv_append(k1, k1, np.arange(5, dtype=np.int32) + PAGE, kp, vp, ks, vs, n_head_kv=Hk,
                   head_dim=d, page_size=PAGE, kv_dtype=orc.KV_FP8)
-    s0 = ks[1, 0]
+    s0 = np.float32(ks[1, 0])
+    c0 = kp[1, 0, :5].copy()
+    # rows that fit keep the scale and the earlier codes
+    half = bf16_round(np.full((1, Hk, d), 0.5))
+    orc.kv_append(half, half, np.array([PAGE + 5], np.int32), kp, vp, ks, vs, n_head_kv=Hk,
+                  head_dim=d, page_size=PAGE, kv_dtype=orc.KV_FP8)
+    assert ks[1, 0] == s0 and (kp[1, 0, :5] == c0).all()
+    c5 = kp[1, 0, 5].copy()
+    # rows that do not fit: the scale doubles until 100 / scale <= 448
     big = bf16_round(np.full((3, Hk, d), 100.0))
-    orc.kv_append(big, big, np.arange(5, 8, dtype=np.int32) + PAGE, kp, vp, ks, vs,
+    orc.kv_append(big, big, np.arange(6, 9, dtype=np.int32) + PAGE, kp, vp, ks, vs,
                   n_head_kv=Hk, head_dim=d, page_size=PAGE, kv_dtype=orc.KV_FP8)
-    assert ks[1, 0] == s0  # offset 0 not written: scale kept
-    assert (kp[1, 0, 5:8] == 0x7E).all()  # saturated
+    s1 = np.float32(ks[1, 0])
+    k = int(round(np.log2(s1 / s0)))
+    assert k >= 1 and s1 == s0 * np.float32(2.0 ** k)
+    assert np.float32(100.0) / s1 <= 448 < np.float32(100.0) / (s1 / np.float32(2))
+    # earlier codes re-encoded at s1: torch's E4M3 conversion of
+    # fp32(fp32(value * s0) / s1), and equal values wherever they stay normal
+    old = np.concatenate([c0, c5[None]])
+    y = (torch_e4m3_value(old).astype(np.float32) * s0) / s1
+    np.testing.assert_array_equal(kp[1, 0, :6], torch_e4m3_encode(y))
+    stays = np.abs(torch_e4m3_value(old)) * 2.0 ** -k >= 2.0 ** -6
+    assert stays.any()
+    np.testing.assert_array_equal((torch_e4m3_value(kp[1, 0, :6]) * float(s1))[stays],
+                                  (torch_e4m3_value(old) * float(s0))[stays])
+    # the new rows are codes of 100 / s1, not saturated
+    np.testing.assert_array_equal(kp[1, 0, 6:9],
+                                  torch_e4m3_encode(np.full((3, d), np.float32(100.0) / s1)))
+    assert not (kp[1, 0, 6:9] == 0x7E).all()
     # a zero page gets scale 1
     z = np.zeros((1, Hk, d), np.uint16)
     orc.kv_append(z, z, np.array([0], np.int32), kp, vp, ks, vs, n_head_kv=Hk, head_dim=d,
                   page_size=PAGE, kv_dtype=orc.KV_FP8)
     assert ks[0, 0] == 1.0 and (kp[0, 0, 0] == 0).all()
+
+
+def test_fp8_pages_filled_one_token_per_call_stay_accurate(orc):
+    """Decode-style appends (one token per sequence per call) against the
+    attention over the unquantised bf16 rows: within the fp8 tolerance."""
+    rng = np.random.default_rng(8)
+    S, C, H, Hk, d = 3, 300, 8, 2, 64
+    n_pages = S * -(-C // PAGE)
+    table = rng.permutation(n_pages).astype(np.int32).reshape(S, -1)
+    k = bf16_round(rng.standard_normal((S, C, Hk, d)))
+    v = bf16_round(rng.standard_normal((S, C, Hk, d)))
+    q = bf16_round(rng.standard_normal((S, 1, H, d)))
+    slot = lambda s, t: table[s, t // PAGE] * PAGE + t % PAGE
+    kb, vb, _, _ = _pools(n_pages, Hk, d, False)
+    kf, vf, ks, vs = _pools(n_pages, Hk, d, True)
+    for t in range(C):
+        sl = np.array([slot(s, t) for s in range(S)], np.int32)
+        orc.kv_append(k[:, t], v[:, t], sl, kb, vb, n_head_kv=Hk, head_dim=d, page_size=PAGE)
+        orc.kv_append(k[:, t], v[:, t], sl, kf, vf, ks, vs, n_head_kv=Hk, head_dim=d,
+                      page_size=PAGE, kv_dtype=orc.KV_FP8)
+    lens = np.full(S, C, np.int32)
+    ref = orc.paged_attention(q, kb, vb, table, lens, n_head=H, n_head_kv=Hk, head_dim=d,
+                              page_size=PAGE)
+    got = orc.paged_attention(q, kf, vf, table, lens, n_head=H, n_head_kv=Hk, head_dim=d,
+                              page_size=PAGE, kv_dtype=orc.KV_FP8, k_scale=ks, v_scale=vs)
+    assert np.abs(got - ref).max() <= 2e-2
 
 
 def test_fp8_attention_matches_sdpa_on_dequantised(orc):
