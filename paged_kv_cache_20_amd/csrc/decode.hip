@@ -490,9 +490,10 @@ __device__ __forceinline__ int fetch_pages(const SplitArgs& a, const Item& it, b
     return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4u, 0, 0);
 }
 
-template <int D, bool FP8, int NT, bool WIN>
+template <int D, bool FP8, int NT, bool WIN, bool SSC>
 __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(SplitArgs a)
 {
+    static_assert(!SSC || FP8, "scalar-unit scales: fp8 only");
     using G = Geo<D, FP8>;
     constexpr int NBUF = Plan<D, FP8, NT>::NBUF;
     constexpr bool PREQ = Plan<D, FP8, NT>::PREQ;
@@ -684,14 +685,43 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
                     rq, qo + 2u * (uint32_t)qk_dmap<D, FP8>(st, kb), 0, 0);
         }
     };
-    // Scales of item I's pages, lane e for page e (zero past the item, for
-    // a page wholly below the item's first key -- a runtime floor may have
-    // released its entry, which may then name any page -- for an entry
-    // outside the pool, and for bf16).  A zero V scale keeps the masked keys'
-    // zero probabilities zero.
+    // fp8 page scales, two ways.  SSC: each tile's K and V page scales by
+    // the scalar unit, issued after the compute that precedes them in the
+    // ring (the scalar counter completes out of order, so a compute's wait
+    // for its own scales waits for every scalar load issued before it) and
+    // used NBUF - 1 tiles later; kept raw with their pages' rows in the
+    // item, the zero for an empty page chosen at the compute.  This frees
+    // the vector memory path of the per-item loads below (two 64-lane loads
+    // touching 64 scattered lines each), but puts a scalar round trip within
+    // one tile of each compute: for calls with many items per wave.
+    const __attribute__((address_space(4))) float* ksp =
+        (const __attribute__((address_space(4))) float*)a.k_scale;
+    const __attribute__((address_space(4))) float* vsp =
+        (const __attribute__((address_space(4))) float*)a.v_scale;
+    float sk[NBUF][2], sv[NBUF][2];  // (SSC) raw scales of each ring tile's pages
+    int sr[NBUF][2];                 // (SSC) rows of those pages in their item
+    auto issue_sc = [&](int slot, const Item& I, int pidv, bool live, int tile) {
+        if constexpr (SSC) {
+            const int e0 = tile * G::KB;
+            const int e1 = G::KB == 2 ? e0 + 1 : e0;
+            int64_t c0, c1;
+            page(I, pidv, live, e0, c0, sr[slot][0]);
+            page(I, pidv, live, e1, c1, sr[slot][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            sk[slot][0] = ksp[c0];
+            sv[slot][0] = vsp[c0];
+            sk[slot][1] = ksp[c1];
+            sv[slot][1] = vsp[c1];
+        }
+    };
+    // Otherwise per item: lane e holds page e's scales (zero past the item,
+    // for a page wholly below the item's first key -- a runtime floor may
+    // have released its entry, which may then name any page -- for an entry
+    // outside the pool, and for bf16).  A zero V scale keeps the masked
+    // keys' zero probabilities zero.
     auto load_scales = [&](float& ks, float& vs, const Item& I, int pidv, bool live) {
         ks = vs = 0.f;
-        if constexpr (FP8) {
+        if constexpr (FP8 && !SSC) {
             const bool ok = live && lane < I.npg && I.t0 + 16 * lane + 16 > I.lo && pidv >= 0 &&
                             (int64_t)pidv < a.n_pages;
             const uint32_t so = ok ? (uint32_t)(pidv * Hk + I.kh) * 4u : kFar;
@@ -733,8 +763,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     load_scales(ksc, vsc, cur, pid, true);
     Raw<D, FP8> buf[NBUF];
 #pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
+    for (int k = 0; k < NBUF - 1; ++k) {
         issue(buf[k], cur, pid, true, k);
+        issue_sc(k, cur, pid, true, k);
+    }
 
     for (;;) {
         // The item after next: geometry and table entries now.
@@ -772,11 +804,21 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             return FP8 ? rdlane_f(ksc, e < npg ? e : 0) * sm_log2 : sm_log2;
         };
         auto vscale = [&](int e) { return FP8 ? rdlane_f(vsc, e < npg ? e : 0) : 1.f; };
-        auto compute = [&](const Raw<D, FP8>& t, int tile) {
+        auto compute = [&](const Raw<D, FP8>& t, int tile, int slot) {
             const int e0 = tile * G::KB;
             const int e1 = G::KB == 2 ? e0 + 1 : e0;
-            compute_tile<D, FP8, NT, WIN>(t, qop, first, last, m, l, O, t0 + KT * tile, kscale(e0),
-                                     kscale(e1), vscale(e0), vscale(e1), kb);
+            if constexpr (SSC) {
+                constexpr int L = G::KB - 1;
+                compute_tile<D, FP8, NT, WIN>(
+                    t, qop, first, last, m, l, O, t0 + KT * tile,
+                    (sr[slot][0] > 0 ? sk[slot][0] : 0.f) * sm_log2,
+                    (sr[slot][L] > 0 ? sk[slot][L] : 0.f) * sm_log2,
+                    sr[slot][0] > 0 ? sv[slot][0] : 0.f, sr[slot][L] > 0 ? sv[slot][L] : 0.f, kb);
+            } else {
+                compute_tile<D, FP8, NT, WIN>(t, qop, first, last, m, l, O, t0 + KT * tile,
+                                              kscale(e0), kscale(e1), vscale(e0), vscale(e1),
+                                              kb);
+            }
         };
 
         // Tiles whose ring successor is still in this item.
@@ -786,7 +828,8 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
                 const int tile = it + k;
                 issue(buf[(k + NBUF - 1) % NBUF], cur, pid, true, tile + NBUF - 1);
                 if (!bad && tile < nt)
-                    compute(buf[k], tile);
+                    compute(buf[k], tile, k);
+                issue_sc((k + NBUF - 1) % NBUF, cur, pid, true, tile + NBUF - 1);
             }
         }
         // The item's last NBUF tiles; the ring moves on to the next item,
@@ -804,7 +847,11 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             else
                 issue(buf[k - 1], nxt, pid_n, has_next, k - 1);
             if (!bad && tile < nt)
-                compute(buf[k], tile);
+                compute(buf[k], tile, k);
+            if (k == 0)
+                issue_sc(NBUF - 1, cur, pid, true, ntp - 1);
+            else
+                issue_sc(k - 1, nxt, pid_n, has_next, k - 1);
         }
 
         // Partials: O rows are slots 4*kb + r; m, l of slot n.  Bounds-checked
@@ -981,8 +1028,8 @@ hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess)
             return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<D, FP8, NT, WIN>, 256,
-                                                         0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<D, FP8, NT, WIN, false>,
+                                                         256, 0);
         if (e != hipSuccess)
             return e;
         // 1024-key splits: one workgroup per CU keeps about as many items per
@@ -1000,11 +1047,25 @@ hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
         blocks = a.max_blocks;
     if (blocks < 1)
         blocks = 1;
+    // Scalar-unit page scales (fp8, four-deep ring) where the waves have many
+    // items each: at least two (sequence, kv head) streams per wave.  Both
+    // forms compute the same bits.
+    constexpr bool CAN_SSC = FP8 && Plan<D, FP8, NT>::NBUF == 4;
+    const bool ssc = CAN_SSC && (int64_t)a.n_seq * Hk * a.slices >= 2 * blocks * kWaves;
     if (a.phase != 2) {
         if (a.ev_start)
             (void)hipEventRecord(a.ev_start, stream);
-        hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN>), dim3((unsigned)blocks), dim3(256), 0,
-                           stream, a);
+        if constexpr (CAN_SSC) {
+            if (ssc)
+                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, true>), dim3((unsigned)blocks),
+                                   dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false>), dim3((unsigned)blocks),
+                                   dim3(256), 0, stream, a);
+        } else {
+            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false>), dim3((unsigned)blocks),
+                               dim3(256), 0, stream, a);
+        }
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
