@@ -113,12 +113,12 @@ def prefill_flops(n_rows, ctx, w):
 
 # The source file each profiled kernel is built from.
 KERNEL_SOURCE = {"split_kernel": "decode.hip", "combine_kernel": "decode.hip",
-                 "prefill_kernel": "prefill.hip"}
+                 "prefill_kernel": "prefill.hip", "prefill_pipe_kernel": "prefill_pipe.hip"}
 
 
 def kernel_source_hash(kernel_key):
     """First 16 hex digits of the sha256 of the kernel's source file."""
-    src = KERNEL_SOURCE[kernel_key.split("_decode")[0].split("_prefill")[0]]
+    src = KERNEL_SOURCE[max((k for k in KERNEL_SOURCE if kernel_key.startswith(k)), key=len)]
     with open(os.path.join(ROOT, "paged_kv_cache_20_amd", "csrc", src), "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
@@ -582,7 +582,8 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
                               "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                              "traffic": traffic_from_profiles("prefill_kernel")}
+                              "traffic": traffic_from_profiles(
+                                  "prefill_pipe_kernel" if not w.kv_fp8 else "prefill_kernel")}
     else:
         st = b.setup_split(name)
         wall, kavg, kmed = b.time_split(st, args.steps, args.warmup)
