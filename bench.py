@@ -428,9 +428,10 @@ class Bench:
 
     def time_prefill_fp8(self, steps=10, warmup=3, rounds=3):
         """The 4,096-row chunk over 28,672 cached rows with an fp8 cache:
-        the plain prefill (bf16 QK^T of the decoded codes) against
-        ATTN_PREFILL_FP8_QK (QK^T on the fp8 matrix unit), kernel medians by
-        the library's kernel timer, best of interleaved rounds."""
+        the plain prefill (bf16 MFMA on the decoded codes) against
+        ATTN_PREFILL_FP8_QK (QK^T on the fp8 matrix unit) and QK | PV (PV on
+        it too), kernel medians by the library's kernel timer, best of
+        interleaved rounds."""
         torch, pa = self.torch, self.pa
         w = self.synth.scaled(self.synth.WORKLOADS["prefill_4096_over_28672"], kv_fp8=True,
                               name="prefill_4096_over_28672_fp8kv")
@@ -439,7 +440,8 @@ class Bench:
         fl = prefill_flops(w.rows, st["C"], w)
         best = {}
         for _ in range(rounds):
-            for bits in (0, pa.ATTN_PREFILL_FP8_QK):
+            for bits in (0, pa.ATTN_PREFILL_FP8_QK,
+                         pa.ATTN_PREFILL_FP8_QK | pa.ATTN_PREFILL_FP8_PV):
                 def call(timer=None):
                     if timer is not None:
                         pa.attn_set_kernel_timer(timer[0], timer[1])
@@ -461,12 +463,15 @@ class Bench:
                 med = kern[len(kern) // 2]
                 best[bits] = min(best.get(bits, med), med)
         res = {}
-        for bits, tag in ((0, "bits0_bf16_qk"), (pa.ATTN_PREFILL_FP8_QK, "qk_fp8")):
+        qkpv = pa.ATTN_PREFILL_FP8_QK | pa.ATTN_PREFILL_FP8_PV
+        for bits, tag in ((0, "bits0_bf16_qk"), (pa.ATTN_PREFILL_FP8_QK, "qk_fp8"),
+                          (qkpv, "qk_pv_fp8")):
             ms = best[bits]
             res[tag] = {"kernel_median_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                         "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
         res["flops_per_launch"] = fl
         res["speedup"] = round(best[0] / best[pa.ATTN_PREFILL_FP8_QK], 3)
+        res["speedup_qk_pv"] = round(best[0] / best[qkpv], 3)
         del st
         torch.cuda.empty_cache()
         return res

@@ -272,6 +272,7 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
 
 /* prefill_fp8 bits of attn_paged_prefill_fp8. */
 #define ATTN_PREFILL_FP8_QK 1
+#define ATTN_PREFILL_FP8_PV 2
 
 /*
  * attn_paged_prefill_fp8 -- attn_paged_prefill with the fp8 switch the
@@ -287,8 +288,22 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
  *                        E4M3 at the smallest power-of-two scale 2^e with
  *                        max|q| <= 448 * 2^e (e >= -117), ties to even.
  *                        Softmax and PV are as in attn_paged_prefill.
+ *   ATTN_PREFILL_FP8_PV  (fp8 cache only) PV runs on the fp8 matrix unit:
+ *                        V with its stored E4M3 codes; each 64-key tile's
+ *                        probabilities p (relative to the row's running
+ *                        maximum, p <= 2^8) times its pages' V scales over
+ *                        2^F -- F the exponent of the tile's largest V scale,
+ *                        so the factors lie in (0, 1] -- rounded to E4M3
+ *                        (nearest, ties to even); the products accumulate in
+ *                        fp32 and are scaled by 2^F; the row sum is of the
+ *                        unrounded p.  Each weight thus carries a relative
+ *                        error of at most 2^-4 (E4M3 normals), so an output
+ *                        element moves by at most 2^-4 times the same
+ *                        softmax average of |v|: far below the fp8
+ *                        tolerance over long contexts, up to about 6% of
+ *                        |v| over a handful of keys.
  *
- * Any other bit, or the QK bit with a bf16 cache, returns
+ * The bits combine.  Any other bit, or a bit with a bf16 cache, returns
  * ATTN_E_UNSUPPORTED.  Layout, limits and errors otherwise as
  * attn_paged_prefill; query elements must be finite.
  */

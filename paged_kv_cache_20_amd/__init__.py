@@ -11,7 +11,7 @@ import importlib
 
 _API = {
     "ATTN_E_ARG", "ATTN_E_DEVICE", "ATTN_E_RANGE", "ATTN_E_SHAPE", "ATTN_E_UNSUPPORTED",
-    "ATTN_E_WORKSPACE", "ATTN_OK", "ATTN_PREFILL_FP8_QK", "EXPORTS", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH", "PAGE_SIZE",
+    "ATTN_E_WORKSPACE", "ATTN_OK", "ATTN_PREFILL_FP8_PV", "ATTN_PREFILL_FP8_QK", "EXPORTS", "KV_BF16", "KV_FP8_E4M3", "LIB_PATH", "PAGE_SIZE",
     "VERIFY_ROWS", "AttnError", "attn_block_table_build", "attn_caps",
     "attn_check_block_table_host", "attn_check_device", "attn_check_lengths_host",
     "attn_kv_append",

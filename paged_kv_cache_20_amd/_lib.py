@@ -28,6 +28,7 @@ ATTN_E_ARG = -1
 ATTN_E_SHAPE = -2
 ATTN_E_UNSUPPORTED = -3
 ATTN_PREFILL_FP8_QK = 1
+ATTN_PREFILL_FP8_PV = 2
 ATTN_E_WORKSPACE = -4
 ATTN_E_RANGE = -5
 ATTN_E_DEVICE = -6

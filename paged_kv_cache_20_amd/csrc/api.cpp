@@ -451,11 +451,12 @@ static int prefill_call(const char* fn, const void* q, int32_t n_rows, const voi
                           out);
     if (rc != ATTN_OK)
         return rc;
-    if (prefill_fp8 & ~ATTN_PREFILL_FP8_QK)
-        return fail(ATTN_E_UNSUPPORTED, "%s: prefill_fp8 bits 0x%x (only ATTN_PREFILL_FP8_QK)",
-                    fn, (unsigned)prefill_fp8);
-    if ((prefill_fp8 & ATTN_PREFILL_FP8_QK) && kv_dtype != ATTN_KV_FP8_E4M3)
-        return fail(ATTN_E_UNSUPPORTED, "%s: ATTN_PREFILL_FP8_QK needs an fp8 cache", fn);
+    if (prefill_fp8 & ~(ATTN_PREFILL_FP8_QK | ATTN_PREFILL_FP8_PV))
+        return fail(ATTN_E_UNSUPPORTED,
+                    "%s: prefill_fp8 bits 0x%x (only ATTN_PREFILL_FP8_QK, ATTN_PREFILL_FP8_PV)", fn,
+                    (unsigned)prefill_fp8);
+    if (prefill_fp8 && kv_dtype != ATTN_KV_FP8_E4M3)
+        return fail(ATTN_E_UNSUPPORTED, "%s: prefill_fp8 bits need an fp8 cache", fn);
     if (n_rows <= 0)
         return fail(ATTN_E_SHAPE, "%s: zero rows is not a call (n_rows = %d)", fn, n_rows);
     if (ctx_len < n_rows)
@@ -495,6 +496,7 @@ static int prefill_call(const char* fn, const void* q, int32_t n_rows, const voi
     a.window = window;
     a.kv_floor = kv_floor;
     a.qk_fp8 = (prefill_fp8 & ATTN_PREFILL_FP8_QK) != 0;
+    a.pv_fp8 = (prefill_fp8 & ATTN_PREFILL_FP8_PV) != 0;
     return from_hip(pa::launch_prefill(a, stream), fn);
 }
 

@@ -117,6 +117,9 @@ struct PrefillArgs {
     // fp8 cache only: QK^T on the fp8 matrix unit, K with its stored codes,
     // each query vector rounded to E4M3 at a power-of-two scale.
     int qk_fp8 = 0;
+    // fp8 cache only: PV on the fp8 matrix unit, V with its stored codes, P
+    // rounded to E4M3 with the tile's V page scales folded in.
+    int pv_fp8 = 0;
     // fp8 cache at head_dim 128: workgroups of four waves (64 query rows),
     // which leave a CU room for a decode workgroup beside them.  A row's
     // arithmetic is the same as with eight.

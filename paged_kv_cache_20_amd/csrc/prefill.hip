@@ -56,6 +56,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS __attribute__((address_space(3)))
 
@@ -190,7 +191,7 @@ struct Staged {
 template <class G>
 __device__ __forceinline__ void stage_load(Staged<G>& st, const uint8_t* pool, const float* scl,
                                            const Blk& b, int key0, int wave, int lane, int raw,
-                                           int* bad)
+                                           int* bad, float none = 1.f)
 {
     int pg, rows;
     resolve_page(b, key0, raw, pg, rows, bad);
@@ -206,9 +207,9 @@ __device__ __forceinline__ void stage_load(Staged<G>& st, const uint8_t* pool, c
             st.c[i] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    // A page past the context gets scale 1 (its keys are masked).
+    // A page past the context gets scale `none` (its keys are masked).
     if constexpr (G::EB == 1)
-        st.s = pg >= 0 ? scl[(int64_t)pg * b.Hk + b.kh] : 1.f;
+        st.s = pg >= 0 ? scl[(int64_t)pg * b.Hk + b.kh] : none;
     else
         st.s = 1.f;
 }
@@ -224,6 +225,30 @@ __device__ __forceinline__ void stage_store_codes(const Staged<G>& st, char* buf
         const int c = i * 64 + lane;
         const int key = wave * G::KPW + c / G::CPR, piece = c % G::CPR;
         *(u32x4*)(buf + key * G::ROWB + (piece ^ swzk<G::CPR>(key)) * 16) = st.c[i];
+    }
+    if (lane == 0 && ((wave * G::KPW) & 15) == 0)
+        sc[(wave * G::KPW) >> 4] = st.s;
+}
+
+// fp8 V kept as codes (PV on the fp8 matrix unit): rows of D bytes, 16-byte
+// chunks swizzled by swzv, which keeps the 8 rows one transposing read
+// gathers (keys 4 kb .. 4 kb + 3 and 16 + the same of a 32-key half) on
+// distinct chunk positions.
+template <int CPR>
+__device__ __forceinline__ int swzv(int key)
+{
+    return (key ^ (key >> 4)) & (CPR - 1);
+}
+
+template <class G>
+__device__ __forceinline__ void stage_store_codes_v(const Staged<G>& st, char* buf, float* sc,
+                                                    int wave, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < G::SCH; ++i) {
+        const int c = i * 64 + lane;
+        const int key = wave * G::KPW + c / G::CPR, piece = c % G::CPR;
+        *(u32x4*)(buf + key * G::ROWB + (piece ^ swzv<G::CPR>(key)) * 16) = st.c[i];
     }
     if (lane == 0 && ((wave * G::KPW) & 15) == 0)
         sc[(wave * G::KPW) >> 4] = st.s;
@@ -279,11 +304,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w)
     return __builtin_bit_cast(float, w & 0xFFFF0000u);
 }
 
-template <int D, bool FP8, int RT, int NW, bool QF8>
+template <int D, bool FP8, int RT, int NW, bool QF8, bool PV8>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
 {
     using G = PGeo<D, FP8, RT, NW>;
     static_assert(!QF8 || (FP8 && RT == 1), "fp8 QK^T: fp8 cache, one row tile per wave");
+    static_assert(!PV8 || (FP8 && RT == 1), "fp8 PV: fp8 cache, one row tile per wave");
     constexpr int QS = D / 128;  // k-steps of the fp8 QK^T (128 d-values each)
     constexpr bool STG = FP8;  // staged through registers (fp8) or LDS-direct (bf16)
     __shared__ __attribute__((aligned(1024))) char s_k0[G::TILEB];
@@ -423,6 +449,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
         m[rt] = neg_inf();
         l[rt] = 0.f;
     }
+    int vexp = 0;  // (PV8) O is held divided by 2^vexp
     const float sm_log2 = kLog2e / __builtin_sqrtf((float)D);
     // Score factor of an fp8 page (times its K scale): with fp8 QK^T the
     // query's power-of-two scale too (exact).
@@ -467,6 +494,25 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int j = 0; j < VBS; ++j)
             voff[j] = vkey * G::ROWL + 16 * ((2 * j + ((n & 3) >> 1)) ^ sw) + (n & 1) * 8;
+    }
+
+    // PV8 V^T reads (ds_read_b64_tr_b8): in each 16-lane group the lanes'
+    // 8-byte chunks form 8 rows of 16 bytes (lanes 2r and 2r + 1) and lane i
+    // receives byte i % 8 of the chunk of lane 2r + i / 8 for r = 0 .. 7.
+    // Lane L of group kb points at key row r = L / 2 of its group's eight
+    // keys (4 kb + r, then 16 + 4 kb + r - 4, in each 32-key half), d-values
+    // 16 jb + 8 (L % 2) .. + 7, so lane i gets V[key r][16 jb + i] for r = 0
+    // .. 7: row i of the V^T operand, keys in the P^T operand's order.
+    int v8row[2] = {0, 0}, v8sw[2] = {0, 0};
+    const int v8half = 8 * (lane & 1);
+    if constexpr (PV8) {
+        const int r = (lane & 15) >> 1;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int key = 32 * hf + (r < 4 ? 4 * kb + r : 16 + 4 * kb + (r - 4));
+            v8row[hf] = key * G::ROWB;
+            v8sw[hf] = swzv<G::CPR>(key);
+        }
     }
 
     // S^T of a tile: [row tile][16-key block]; two sets, current and next.
@@ -515,6 +561,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
     // whose first key is tile0 + wk.
     const int wk = ((wave * G::KPW) >> 4) * 16;
     Staged<G> stk, stv;
+    // PV8: V stays as codes; a page with no rows gets V scale 0, so it does
+    // not enter a tile's scale exponent below.
+    constexpr float kNoV = PV8 ? 0.f : 1.f;
+    auto store_v = [&](char* buf, float* sc) {
+        if constexpr (PV8)
+            stage_store_codes_v<G>(stv, buf, sc, wave, lane);
+        else
+            stage_store<G>(stv, buf, sc, wave, lane);
+    };
     auto store_k = [&](char* buf, float* sc) {
         if constexpr (QF8)
             stage_store_codes<G>(stk, buf, sc, wave, lane);
@@ -527,8 +582,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
     if constexpr (STG) {
         stage_load<G>(stk, kp, a.k_scale, b, k0 + wk, wave, lane, rawv, &bad);
         store_k(s_k0, s_ksc[0]);
-        stage_load<G>(stv, vp, a.v_scale, b, k0 + wk, wave, lane, rawv, &bad);
-        stage_store<G>(stv, s_v0, s_vsc[0], wave, lane);
+        stage_load<G>(stv, vp, a.v_scale, b, k0 + wk, wave, lane, rawv, &bad, kNoV);
+        store_v(s_v0, s_vsc[0]);
         if (nt > ts + 1) {
             stage_load<G>(stk, kp, a.k_scale, b, k0 + kKT + wk, wave, lane, rawk, &bad);
             store_k(s_k1, s_ksc[1]);
@@ -558,7 +613,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
         const int tile0 = t * kKT;
         if (t + 1 < nt) {
             if constexpr (STG)
-                stage_load<G>(stv, vp, a.v_scale, b, tile0 + kKT + wk, wave, lane, rawv, &bad);
+                stage_load<G>(stv, vp, a.v_scale, b, tile0 + kKT + wk, wave, lane, rawv, &bad,
+                              kNoV);
             else
                 issue_direct<G>(vwb, vp, b, tile0 + kKT + wk, wave, loff, rawv, &bad);
         }
@@ -627,6 +683,30 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
             }
         }
 
+        // PV8: the tile's V page scales join P before its E4M3 rounding as
+        // vs / 2^F, F the exponent of the tile's largest scale (so every
+        // factor lies in (0, 1] and a probability keeps its E4M3 precision);
+        // O is held divided by 2^F and moved exactly when F changes.
+        float fac[4];
+        if constexpr (PV8) {
+            const float vmax = fmaxf(fmaxf(vrs[0], vrs[1]), fmaxf(vrs[2], vrs[3]));
+            int f = vexp;
+            if (vmax > 0.f)
+                (void)__builtin_frexpf(vmax, &f);
+            if (f != vexp) {
+                const float mv = __builtin_ldexpf(1.f, vexp - f);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int jb = 0; jb < G::DBLK; ++jb)
+                        O[rt][jb] = O[rt][jb] * mv;
+                vexp = f;
+            }
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+                fac[kq] = __builtin_ldexpf(vrs[kq], -vexp);
+        }
+
         // Scores of tile t+1 (on stale K past the last tile: never used),
         // interleaved with tile t's probabilities.
         float muse[RT];
@@ -638,7 +718,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
         for (int kq = 0; kq < 4; ++kq) {
             scores(kr, nxt, kq);
             kn[kq] = FP8 ? krs[kq] : 1.f;
-            const float vsc = FP8 ? vrs[kq] : 1.f;
+            const float vsc = PV8 ? fac[kq] : FP8 ? vrs[kq] : 1.f;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 float pe[4];
@@ -653,6 +733,45 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
                 l[rt] = l[rt] + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
             }
         }
+        if constexpr (PV8) {
+            // P^T as E4M3 (nearest, ties to even): byte j of the 32-key half
+            // hf is key 32 hf + 16 (j / 4) + 4 kb + j % 4, the key whose V
+            // the transposing read puts in byte j of the V^T operand.
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                i32x2 p8[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(e[rt][2 * hf][0], e[rt][2 * hf][1], 0,
+                                                             false);
+                    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(e[rt][2 * hf][2], e[rt][2 * hf][3], w0,
+                                                         true);
+                    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(e[rt][2 * hf + 1][0],
+                                                             e[rt][2 * hf + 1][1], 0, false);
+                    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(e[rt][2 * hf + 1][2],
+                                                         e[rt][2 * hf + 1][3], w1, true);
+                    p8[rt] = i32x2{w0, w1};
+                }
+                constexpr int NB = 4;  // d blocks per batch of V reads
+#pragma unroll
+                for (int j0 = 0; j0 < G::DBLK; j0 += NB) {
+                    i32x2 va[NB];
+#pragma unroll
+                    for (int jj = 0; jj < NB; ++jj) {
+                        const int jb = j0 + jj;
+                        va[jj] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (LDS i32x2*)(vr + v8row[hf] + ((jb ^ v8sw[hf]) << 4) + v8half));
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < NB; ++jj)
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            O[rt][j0 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                                __builtin_bit_cast(long, va[jj]), __builtin_bit_cast(long, p8[rt]),
+                                O[rt][j0 + jj], 0, 0, 0);
+                }
+            }
+        } else {
         // P^T operands: k index i of the 32-key half hf is key
         // 32 hf + 16 (i / 4) + 4 kb + i % 4, matching the V^T reads.
         u32x4 pb[RT][2];
@@ -693,10 +812,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
                             __builtin_bit_cast(bf16x8, pb[rt][hf]), O[rt][j0 + jj], 0, 0, 0);
             }
         }
+        }
 
         if constexpr (STG) {
             if (t + 1 < nt)
-                stage_store<G>(stv, vwb, vws, wave, lane);
+                store_v(vwb, vws);
             if (t + 2 < nt)
                 store_k(kwb, kws);
         } else {
@@ -718,7 +838,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
     const bool nan = s_bad != 0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const float inv = 1.f / row_sum4(l[rt]);
+        const float inv = PV8 ? __builtin_ldexpf(1.f / row_sum4(l[rt]), vexp)
+                              : 1.f / row_sum4(l[rt]);
         if (row[rt] >= n_rows)
             continue;
         uint16_t* out = (uint16_t*)a.out + ((tok0 + row[rt]) * H + head[rt]) * D;
@@ -733,7 +854,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
     }
 }
 
-template <int D, bool FP8, int RT, int NW, bool QF8 = false>
+template <int D, bool FP8, int RT, int NW, bool QF8 = false, bool PV8 = false>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream)
 {
     using G = PGeo<D, FP8, RT, NW>;
@@ -746,7 +867,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream)
     const int grid = (int)((nblk + 7) / 8) * 8;
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, stream);
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, RT, NW, QF8>), dim3(grid), dim3(G::NTH), 0, stream,
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, RT, NW, QF8, PV8>), dim3(grid), dim3(G::NTH), 0, stream,
                        a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.ev_stop)
@@ -765,13 +886,24 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
     // wave's softmax overlaps the other's matrix work.  (Two row tiles per
     // wave halve the LDS reads per flop but need more than the 256 VGPRs of
     // a wave at this occupancy for head_dim 256.)
-    if (a.qk_fp8) {
+    if (a.qk_fp8 || a.pv_fp8) {
         if (!a.fp8)
             return hipErrorNotSupported;
-        if (a.head_dim == 128)
-            return launch_t<128, true, 1, 8, true>(a, stream);
-        if (a.head_dim == 256)
-            return launch_t<256, true, 1, 8, true>(a, stream);
+        const int sel = (a.qk_fp8 ? 1 : 0) | (a.pv_fp8 ? 2 : 0);
+        if (a.head_dim == 128) {
+            switch (sel) {
+            case 1: return launch_t<128, true, 1, 8, true, false>(a, stream);
+            case 2: return launch_t<128, true, 1, 8, false, true>(a, stream);
+            default: return launch_t<128, true, 1, 8, true, true>(a, stream);
+            }
+        }
+        if (a.head_dim == 256) {
+            switch (sel) {
+            case 1: return launch_t<256, true, 1, 8, true, false>(a, stream);
+            case 2: return launch_t<256, true, 1, 8, false, true>(a, stream);
+            default: return launch_t<256, true, 1, 8, true, true>(a, stream);
+            }
+        }
         return hipErrorNotSupported;
     }
     if (a.narrow && a.fp8 && a.head_dim == 128)

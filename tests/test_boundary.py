@@ -291,8 +291,9 @@ def test_host_checkers(pa):
 
 
 @pytest.mark.parametrize("over,code,needle", [
-    (dict(prefill_fp8=2), -3, "prefill_fp8 bits 0x2"),
-    (dict(prefill_fp8=1), -3, "needs an fp8 cache"),
+    (dict(prefill_fp8=4), -3, "prefill_fp8 bits 0x4"),
+    (dict(prefill_fp8=1), -3, "need an fp8 cache"),
+    (dict(prefill_fp8=2), -3, "need an fp8 cache"),
     (dict(prefill_fp8=1, kv_dtype=1, k_scale=FAKE, v_scale=FAKE, n_rows=0), -2, "zero rows"),
     (dict(prefill_fp8=1, kv_dtype=1, k_scale=None, v_scale=None), -1, "fp8 kv needs"),
     (dict(prefill_fp8=0, ctx_len=40000), -5, "exceeds"),
