@@ -64,6 +64,10 @@ def _load():
         lib.oracle_paged_attention_window.restype = ctypes.c_int
         lib.oracle_kv_append.argtypes = [P, P, P, i32, P, P, P, P, i64, i32, i32, i32, i32]
         lib.oracle_kv_append.restype = ctypes.c_int
+        lib.oracle_tree_view.argtypes = [
+            P, P, P, P, i64, P, i32, i32, i32, ctypes.c_uint32, i32, i32, i32, i32, i32,
+            P, P, P, P, i32]
+        lib.oracle_tree_view.restype = ctypes.c_int
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -150,6 +154,35 @@ def kv_append(k_new, v_new, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=
                               page_size, kv_dtype)
     if rc != 0:
         raise ValueError("oracle_kv_append failed with %d" % rc)
+
+
+def tree_view(k_pool, v_pool, k_scale, v_scale, table_row, ctx_len, rows, mask, r, *,
+              n_head_kv, head_dim, page_size, kv_dtype=KV_BF16):
+    """The cache row ``r`` of a tree-shaped round attends: its branch laid out
+    as a plain sequence in ``ceil(L / page_size)`` private pages (identity
+    block table).  Returns ``(k, v, k_scale, v_scale, L)`` (scales None for
+    bf16).  See ``oracle_tree_view`` in attn_oracle.c for the rule."""
+    lib = _load()
+    tab = _c(table_row, np.int32)
+    for a in (k_pool, v_pool) + ((k_scale, v_scale) if kv_dtype == KV_FP8 else ()):
+        assert a.flags.c_contiguous
+    el = np.uint16 if kv_dtype == KV_BF16 else np.uint8
+    assert k_pool.dtype == el and v_pool.dtype == el
+    n_rows = ctx_len - rows + bin(int(mask) & ((1 << rows) - 1)).count("1")
+    npg = max(1, -(-n_rows // page_size))
+    shape = (npg, n_head_kv, page_size, head_dim)
+    k2, v2 = np.zeros(shape, el), np.zeros(shape, el)
+    ks2 = vs2 = None
+    if kv_dtype == KV_FP8:
+        ks2 = np.zeros((npg, n_head_kv), np.float32)
+        vs2 = np.zeros((npg, n_head_kv), np.float32)
+    rc = lib.oracle_tree_view(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                              k_pool.shape[0], _ptr(tab), tab.shape[0], int(ctx_len), int(rows),
+                              int(mask) & 0xFFFFFFFF, int(r), n_head_kv, head_dim, page_size,
+                              kv_dtype, _ptr(k2), _ptr(v2), _ptr(ks2), _ptr(vs2), npg)
+    if rc < 0:
+        raise ValueError("oracle_tree_view failed with %d" % rc)
+    return k2, v2, ks2, vs2, rc
 
 
 def round_q_e4m3(q, return_exps=False):

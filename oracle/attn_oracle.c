@@ -484,3 +484,141 @@ int oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new,
     }
     return 0;
 }
+
+/*
+ * oracle_tree_view -- the cache that row r of a tree-shaped speculative round
+ * attends ("Radiance Architecture Plugins -- declaring a model", section
+ * "Declare: drafters, encoders, generators": a drafter may propose a tree;
+ * "TandemLLM -- Adding a model", section "The adapter path in ten steps": a
+ * recorded decode replayed as trees must match row for row).
+ *
+ *   pools, scales  the cache, as for oracle_paged_attention
+ *   table_row      the sequence's block-table row (max_pages entries)
+ *   ctx_len, rows  C and R: the round's rows sit at C0 .. C0 + R - 1, C0 = C - R
+ *   mask, r        bit j set = row r attends round row j; a valid mask names r
+ *                  and no later row
+ *   out_*          the view: pages 0 .. out_pages - 1 of a private cache whose
+ *                  block table is the identity; slots past the view's length
+ *                  are zero
+ *
+ * The view holds the context positions 0 .. C0 - 1 followed by the round rows
+ * the mask names, in row order, at C0, C0 + 1, ... (the branch laid out as a
+ * plain sequence).  bf16: every token's bytes are copied.  fp8: a view page
+ * takes the scale of the cache page that holds its first token (its home
+ * page); tokens from the home page keep their codes; a token from another
+ * page (possible only where a round crosses a page boundary and the branch
+ * skips rows, so a later row moves down into the earlier page) is written as
+ * kv_append would write a new row into that page at a later call: its value
+ * y = fp32(value(code) * its page's scale) is encoded at the view page's
+ * scale, which first doubles while fp32 absmax(y) / scale > 448 (the home
+ * tokens are then re-encoded too, code' = nearest E4M3 to fp32(fp32(value *
+ * s) / s')).  A chain mask therefore gives the cache itself, byte for byte.
+ *
+ * Returns the view's length, -1 for an invalid mask or length, -2 for a page
+ * outside the pool, -3 when out_pages is too small.
+ */
+int oracle_tree_view(const void *k_pool, const void *v_pool, const float *k_scale,
+                     const float *v_scale, int64_t n_pages, const int32_t *table_row,
+                     int max_pages, int ctx_len, int rows, uint32_t mask, int r, int n_head_kv,
+                     int head_dim, int page_size, int kv_dtype, void *out_k, void *out_v,
+                     float *out_ks, float *out_vs, int out_pages)
+{
+    const int P = page_size, d = head_dim, Hk = n_head_kv;
+    if (rows < 1 || rows > 32 || r < 0 || r >= rows || ctx_len < rows ||
+        (int64_t)ctx_len > (int64_t)max_pages * P)
+        return -1;
+    if (!(mask >> r & 1u) || (r + 1 < 32 && (mask >> (r + 1)) != 0))
+        return -1;
+    const int C0 = ctx_len - rows;
+    int L = C0;
+    for (int j = 0; j < rows; ++j)
+        L += (int)(mask >> j & 1u);
+    const int npg = (L + P - 1) / P;
+    if (npg > out_pages)
+        return -3;
+    /* pos[t]: cache position of view position t */
+    int *pos = (int *)malloc(sizeof(int) * (size_t)L);
+    for (int t = 0; t < C0; ++t)
+        pos[t] = t;
+    for (int j = 0, t = C0; j < rows; ++j)
+        if (mask >> j & 1u)
+            pos[t++] = C0 + j;
+    for (int t = 0; t < L; ++t) {
+        const int32_t pg = table_row[pos[t] / P];
+        if (pg < 0 || (int64_t)pg >= n_pages) {
+            free(pos);
+            return -2;
+        }
+    }
+    const size_t eb = kv_dtype == ORC_KV_BF16 ? 2 : 1;
+    const int64_t row_el = d, page_el = (int64_t)Hk * P * d;
+    memset(out_k, 0, eb * (size_t)(out_pages * page_el));
+    memset(out_v, 0, eb * (size_t)(out_pages * page_el));
+    if (kv_dtype == ORC_KV_BF16) {
+        for (int t = 0; t < L; ++t) {
+            const int64_t sp = table_row[pos[t] / P], so = pos[t] % P;
+            for (int h = 0; h < Hk; ++h)
+                for (int i = 0; i < d; ++i) {
+                    const int64_t src = (sp * Hk + h) * P * row_el + so * row_el + i;
+                    const int64_t dst = ((int64_t)(t / P) * Hk + h) * P * row_el + (t % P) * row_el + i;
+                    ((uint16_t *)out_k)[dst] = ((const uint16_t *)k_pool)[src];
+                    ((uint16_t *)out_v)[dst] = ((const uint16_t *)v_pool)[src];
+                }
+        }
+        free(pos);
+        return L;
+    }
+    for (int kv = 0; kv < 2; ++kv) {
+        const uint8_t *pool = (const uint8_t *)(kv ? v_pool : k_pool);
+        const float *scale = kv ? v_scale : k_scale;
+        uint8_t *out = (uint8_t *)(kv ? out_v : out_k);
+        float *out_s = kv ? out_vs : out_ks;
+        for (int vp = 0; vp < npg; ++vp) {
+            const int t_lo = vp * P, t_hi = L < t_lo + P ? L : t_lo + P;
+            const int64_t home = table_row[pos[t_lo] / P];
+            for (int h = 0; h < Hk; ++h) {
+                const float s_home = scale[home * Hk + h];
+                /* absmax of the moved tokens' values */
+                float a = 0.0f;
+                for (int t = t_lo; t < t_hi; ++t) {
+                    const int64_t sp = table_row[pos[t] / P];
+                    if (sp == home)
+                        continue;
+                    const float s = scale[sp * Hk + h];
+                    for (int i = 0; i < d; ++i) {
+                        const uint8_t c = pool[((sp * Hk + h) * P + pos[t] % P) * row_el + i];
+                        const float y = fabsf((float)oracle_e4m3_value(c) * s);
+                        if (y > a)
+                            a = y;
+                    }
+                }
+                float s_view = s_home;
+                if (a <= 3.4028234663852886e38f && a / s_home > 448.0f)
+                    while (a / s_view > 448.0f)
+                        s_view = s_view * 2.0f;
+                const int grown = s_view != s_home;
+                for (int t = t_lo; t < t_hi; ++t) {
+                    const int64_t sp = table_row[pos[t] / P];
+                    const float s = scale[sp * Hk + h];
+                    const int moved = sp != home;
+                    for (int i = 0; i < d; ++i) {
+                        const uint8_t c = pool[((sp * Hk + h) * P + pos[t] % P) * row_el + i];
+                        uint8_t c2 = c;
+                        if (moved || grown) {
+                            const float y = (float)oracle_e4m3_value(c) * s;
+                            c2 = oracle_e4m3_encode(y / s_view);
+                        }
+                        out[(((int64_t)vp * Hk + h) * P + (t % P)) * row_el + i] = c2;
+                    }
+                }
+                out_s[(int64_t)vp * Hk + h] = s_view;
+            }
+        }
+        /* pages of the view past its length keep scale 1 */
+        for (int vp = npg; vp < out_pages; ++vp)
+            for (int h = 0; h < Hk; ++h)
+                out_s[(int64_t)vp * Hk + h] = 1.0f;
+    }
+    free(pos);
+    return L;
+}
