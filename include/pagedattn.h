@@ -230,9 +230,14 @@ int attn_paged_verify_width(const void* q, const void* k_pool, const void* v_poo
  * order; its result equals, bit for bit, attn_paged_decode of the same row
  * over a cache holding the context followed by those rows at positions C0,
  * C0 + 1, ... (its branch).  A chain mask (row r names 0 .. r) gives the
- * attn_paged_verify_width rows.  Bytes are copied into the views, never
- * re-quantised, so with an fp8 pool a round must lie inside one page (one
- * scale); rows of a round that does not get NaN.  Needs n_seq * width <=
+ * attn_paged_verify_width rows.  bf16 bytes are copied into the views.
+ * With an fp8 pool a view page takes the scale of the cache page holding its
+ * first token and that page's codes; rows that move down into it from the
+ * next page (a round across a page boundary whose branch skips rows) are
+ * written as attn_kv_append would write them there at a later call: each
+ * value (code times its page's scale, fp32) is encoded at the view page's
+ * scale, doubled first while those values exceed 448 times it (the page's
+ * other codes are then re-encoded too).  Needs n_seq * width <=
  * 4096 and at most 16 query heads per kv head.  The context below the
  * split holding C0 (splits of 1024 keys with an fp8 cache at head_dim 128,
  * else 512) is read once for all rows of a sequence (as by

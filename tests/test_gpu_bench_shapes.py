@@ -11,7 +11,7 @@ import oracle
 import paged_kv_cache_20_amd as pa
 from paged_kv_cache_20_amd import synth
 from gpu_util import PAGE, TOL, GpuCache, OracleCache, max_err, say
-from test_gpu_tree import branch_positions, oracle_branch, run_tree, scratch_for
+from test_gpu_tree import oracle_view, oracle_view_attention, run_tree, scratch_for
 
 pytestmark = pytest.mark.gpu
 
@@ -94,12 +94,10 @@ def test_tree8_on_the_verify_workload(verify_cache):
     out = run_tree(gpu, inp, masks, scratch_for(inp))
     assert torch.isfinite(out.float()).all()
     oc = OracleCache(inp)
-    lens = inp.lengths.cpu().numpy()
     worst = 0.0
     for s in (0, 31):
         for r in range(8):
-            pos = branch_positions(int(lens[s]), 8, int(masks[s, r]))
-            ref = oracle_branch(oc, inp, s, r, pos)
+            ref = oracle_view_attention(inp, s, r, oracle_view(oc, inp, s, r, int(masks[s, r])))
             worst = max(worst, float(np.max(np.abs(out[s, r].float().cpu().double().numpy()
                                                    - ref))))
     say("[gpu] tree8 sampled seqs 0, 31 max abs err", worst)

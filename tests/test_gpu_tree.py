@@ -1,10 +1,12 @@
 """GPU parity of tree-shaped speculative rounds (MI355X only).
 
 Row r of a round attends the cached context plus the round rows its mask
-names.  Each tree row must equal, bit for bit, the GPU decode of the same
-row over its branch laid out contiguously (the same stored bytes copied to
-fresh pages), and lie within tolerance of the CPU oracle over the branch
-built from the oracle's own cache.  A chain mask gives the width-R round.
+names.  The oracle lays that branch out as a plain sequence (oracle.tree_view:
+bytes copied; with fp8, rows moved down into the previous page re-encoded at
+its scale).  Each tree row must equal, bit for bit, the GPU decode of the same
+row over that view, and lie within tolerance of the CPU oracle over it; the
+view pages the call builds must equal the oracle's byte for byte.  A chain
+mask gives the width-R round.
 """
 import numpy as np
 import pytest
@@ -62,25 +64,23 @@ def branch_positions(C, R, mask):
     return list(range(C0)) + [C0 + j for j in range(R) if mask >> j & 1]
 
 
-def gpu_branch_decode(gpu, inp, s, r, pos):
-    """Decode of row (s, r) over its branch copied byte for byte to new pages."""
+def oracle_view(oc, inp, s, r, mask):
     w = inp.w
-    n = len(pos)
-    npg = -(-n // PAGE)
-    tab = inp.table[s].long()
-    p = torch.tensor(pos, device="cuda")
-    src_page, src_row = tab[p // PAGE], p % PAGE
-    shape = (npg, w.n_head_kv, PAGE, w.head_dim)
-    k2 = torch.zeros(shape, dtype=gpu.k.dtype, device="cuda")
-    v2 = torch.zeros(shape, dtype=gpu.v.dtype, device="cuda")
-    dst = torch.arange(n, device="cuda")
-    k2[dst // PAGE, :, dst % PAGE, :] = gpu.k[src_page, :, src_row, :]
-    v2[dst // PAGE, :, dst % PAGE, :] = gpu.v[src_page, :, src_row, :]
-    ks2 = vs2 = None
-    if gpu.ks is not None:
-        first = src_page[torch.arange(npg, device="cuda") * PAGE]
-        ks2 = gpu.ks[first].contiguous()
-        vs2 = gpu.vs[first].contiguous()
+    R = inp.q.shape[1]
+    return oracle.tree_view(oc.k, oc.v, oc.ks, oc.vs, oc.table[s], int(oc.lens[s]), R, mask, r,
+                            n_head_kv=w.n_head_kv, head_dim=w.head_dim, page_size=PAGE,
+                            kv_dtype=oracle.KV_FP8 if w.kv_fp8 else oracle.KV_BF16)
+
+
+def gpu_view_decode(gpu, inp, s, r, view):
+    """GPU decode of row (s, r) over the oracle's view of its branch."""
+    w = inp.w
+    k2, v2, ks2, vs2, n = view
+    npg = k2.shape[0]
+    k2 = torch.from_numpy(k2).cuda().view(gpu.k.dtype)
+    v2 = torch.from_numpy(v2).cuda().view(gpu.v.dtype)
+    if ks2 is not None:
+        ks2, vs2 = torch.from_numpy(ks2).cuda(), torch.from_numpy(vs2).cuda()
     table = torch.arange(npg, dtype=torch.int32, device="cuda").view(1, npg)
     lens = torch.tensor([n], dtype=torch.int32, device="cuda")
     q = inp.q[s, r].reshape(1, 1, w.n_head, w.head_dim).contiguous()
@@ -93,28 +93,40 @@ def gpu_branch_decode(gpu, inp, s, r, pos):
     return out[0, 0]
 
 
-def oracle_branch(oc, inp, s, r, pos):
-    """The oracle over the branch copied from the oracle's own cache."""
+def oracle_view_attention(inp, s, r, view):
     w = inp.w
-    n = len(pos)
-    npg = -(-n // PAGE)
-    tab = oc.table[s]
-    p = np.asarray(pos)
-    sp, sr = tab[p // PAGE], p % PAGE
-    k2 = np.zeros((npg, w.n_head_kv, PAGE, w.head_dim), oc.k.dtype)
-    v2 = np.zeros_like(k2)
-    i = np.arange(n)
-    k2[i // PAGE, :, i % PAGE, :] = oc.k[sp, :, sr, :]
-    v2[i // PAGE, :, i % PAGE, :] = oc.v[sp, :, sr, :]
-    ks2 = vs2 = None
-    if oc.ks is not None:
-        first = sp[np.arange(npg) * PAGE]
-        ks2, vs2 = oc.ks[first], oc.vs[first]
+    k2, v2, ks2, vs2, n = view
+    npg = k2.shape[0]
     q = synth.bits(inp.q[s, r]).reshape(1, 1, w.n_head, w.head_dim)
     return oracle.paged_attention(
         q, k2, v2, np.arange(npg, dtype=np.int32).reshape(1, npg), np.array([n], np.int32),
         n_head=w.n_head, n_head_kv=w.n_head_kv, head_dim=w.head_dim, page_size=PAGE,
         kv_dtype=oracle.KV_FP8 if w.kv_fp8 else oracle.KV_BF16, k_scale=ks2, v_scale=vs2)[0, 0]
+
+
+def check_view_pages(gpu, inp, s, r, scratch, view):
+    """The call's private pages hold the oracle's view pages of the round
+    (rows below the view's length; scales with fp8)."""
+    k2, v2, ks2, vs2, n = view
+    R = inp.q.shape[1]
+    tp = (int(inp.lengths[s]) - R) // PAGE
+    for i, vp in enumerate(range(tp, k2.shape[0])):
+        pg = int(scratch[s, r, i])
+        rows = min(PAGE, n - vp * PAGE)
+        for pool, ref in ((gpu.k, k2), (gpu.v, v2)):
+            got = pool[pg, :, :rows].contiguous().view(torch.uint8).cpu().numpy()
+            want = np.ascontiguousarray(ref[vp, :, :rows]).view(np.uint8)
+            np.testing.assert_array_equal(got, want, err_msg=str((s, r, vp)))
+        if ks2 is not None:
+            np.testing.assert_array_equal(gpu.ks[pg].cpu().numpy(), ks2[vp])
+            np.testing.assert_array_equal(gpu.vs[pg].cpu().numpy(), vs2[vp])
+
+
+def moved_rows(C, R, mask):
+    """Round rows of the branch that land in an earlier page than their own."""
+    C0 = C - R
+    js = [j for j in range(R) if mask >> j & 1]
+    return sum(1 for i, j in enumerate(js) if (C0 + j) // PAGE > (C0 + i) // PAGE)
 
 
 CASES = [
@@ -127,6 +139,10 @@ CASES = [
     tree_workload("tr_bf16_d128_g16_w8", [9, 515, 1030], 8, 32, 2, 128, False, 116),
     # fp8: every round inside one page (C0 % 16 + R <= 16: 0, 3, 0, 0)
     tree_workload("tr_fp8_d128_g4", [8, 523, 1000, 4104], 8, 32, 8, 128, True, 113),
+    # fp8 rounds across a page boundary (C0 % 16 = 4, 11, 5, 10): branches
+    # that skip rows move later rows down into the page of C0
+    tree_workload("tr_fp8_d128_cross", [60, 531, 1037, 2050], 8, 32, 8, 128, True, 114),
+    tree_workload("tr_fp8_d256_cross_w5", [33, 707, 1298], 5, 16, 4, 256, True, 117),
 ]
 
 
@@ -143,21 +159,28 @@ def test_tree_rows_equal_branch_decodes_and_oracle(case):
     w, inp, gpu = case
     S, R = inp.q.shape[0], inp.q.shape[1]
     masks = random_masks(S, R, 7)
-    out = run_tree(gpu, inp, masks, scratch_for(inp))
+    scratch = scratch_for(inp)
+    out = run_tree(gpu, inp, masks, scratch)
     oc = OracleCache(inp)
     oc.check_pools_equal(gpu)
     lens = inp.lengths.cpu().numpy()
-    worst = -1.0
+    sc = scratch.cpu().numpy()
+    worst, moved = -1.0, 0
     for s in range(S):
         for r in range(R):
-            pos = branch_positions(int(lens[s]), R, int(masks[s, r]))
-            dec = gpu_branch_decode(gpu, inp, s, r, pos)
+            view = oracle_view(oc, inp, s, r, int(masks[s, r]))
+            assert view[4] == len(branch_positions(int(lens[s]), R, int(masks[s, r])))
+            check_view_pages(gpu, inp, s, r, sc, view)
+            dec = gpu_view_decode(gpu, inp, s, r, view)
             assert same_bits(dec, out[s, r]), (s, r)
-            ref = oracle_branch(oc, inp, s, r, pos)
+            ref = oracle_view_attention(inp, s, r, view)
             ex = excess_err(out[s, r], ref, TOL[w.kv_fp8])
             worst = max(worst, ex)
             assert ex <= 0, (s, r)
-    say("[gpu]", w.name, "worst excess", worst)
+            moved += moved_rows(int(lens[s]), R, int(masks[s, r]))
+    if "cross" in w.name:
+        assert moved > 0
+    say("[gpu]", w.name, "worst excess", worst, "moved rows", moved)
 
 
 def test_chain_tree_is_the_width_round(case):
@@ -197,10 +220,42 @@ def test_bad_mask_gives_nan_row_only(case):
     assert same_bits(out[keep.cuda()], good[keep.cuda()])
 
 
-def test_fp8_round_across_a_page_gives_nan():
-    w = tree_workload("tr_fp8_cross", [60, 531], 8, 8, 2, 128, True, 114)  # C0 % 16 = 4, 11
+def test_fp8_moved_rows_grow_the_view_scale():
+    """Rows moved down from a page with a much larger scale grow the view
+    page's scale (the page's other codes re-encoded); the view pages equal the
+    oracle's, and each row the decode over that view."""
+    w = tree_workload("tr_fp8_grow", [68, 531, 2050], 8, 16, 4, 128, True, 118)  # C0 % 16 = 12, 11, 10
     inp = synth.draw(w, "cuda")
     gpu = GpuCache(inp)
-    out = run_tree(gpu, inp, random_masks(2, 8, 3), scratch_for(inp))
-    assert torch.isnan(out[1].float()).all()       # 523 % 16 = 11: 11 + 8 > 16
-    assert torch.isfinite(out[0].float()).all()    # 52 % 16 = 4: inside one page
+    oc = OracleCache(inp)
+    S, R = 3, 8
+    lens = inp.lengths.cpu().numpy()
+    tab = inp.table.cpu().numpy()
+    for s in range(S):
+        tp = (int(lens[s]) - R) // PAGE
+        # the same change to both caches: the next page's values 8x (K), 1.37x (V)
+        gpu.ks[int(tab[s, tp + 1])] *= 8.0
+        gpu.vs[int(tab[s, tp + 1])] *= 1.37
+        oc.ks[oc.table[s, tp + 1]] *= np.float32(8.0)
+        oc.vs[oc.table[s, tp + 1]] *= np.float32(1.37)
+    oc.check_pools_equal(gpu)
+    masks = np.zeros((S, R), np.int32)
+    for s in range(S):
+        for r in range(R):
+            masks[s, r] = (1 << r) | (1 if r > 0 else 0)  # every row's parent is row 0
+    scratch = scratch_for(inp)
+    out = run_tree(gpu, inp, masks, scratch)
+    sc = scratch.cpu().numpy()
+    grown = 0
+    for s in range(S):
+        C0 = int(lens[s]) - R
+        tp = C0 // PAGE
+        for r in range(R):
+            view = oracle_view(oc, inp, s, r, int(masks[s, r]))
+            check_view_pages(gpu, inp, s, r, sc, view)
+            assert same_bits(gpu_view_decode(gpu, inp, s, r, view), out[s, r]), (s, r)
+            ex = excess_err(out[s, r], oracle_view_attention(inp, s, r, view), TOL[True])
+            assert ex <= 0, (s, r)
+            if (C0 + r) // PAGE > tp:  # row r moved next to row 0
+                grown += int((view[2][tp] != oc.ks[oc.table[s, tp]]).any())
+    assert grown > 0
