@@ -294,8 +294,10 @@ int attn_paged_prefill(const void* q, int32_t n_rows, const void* k_pool, const 
  *                        max|q| <= 448 * 2^e (e >= -117), ties to even.
  *                        Softmax and PV are as in attn_paged_prefill.
  *   ATTN_PREFILL_FP8_PV  (fp8 cache only) PV runs on the fp8 matrix unit:
- *                        V with its stored E4M3 codes; each 64-key tile's
- *                        probabilities p (relative to the row's running
+ *                        V with its stored E4M3 codes; each key tile's
+ *                        (32 keys with both bits at head_dim 128 or 256 and
+ *                        g dividing 128, else 64) probabilities p
+ *                        (relative to the row's running
  *                        maximum, p <= 2^8) times its pages' V scales over
  *                        2^F -- F the exponent of the tile's largest V scale,
  *                        so the factors lie in (0, 1] -- rounded to E4M3

@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "qround.h"
 
 
 namespace pa {
@@ -297,13 +298,6 @@ __device__ __forceinline__ float row_sum4(float v)
     return v + __shfl_xor(v, 32, 64);
 }
 
-// Two bf16 (a dword) to floats.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w)
-{
-    return __builtin_bit_cast(float, w & 0xFFFF0000u);
-}
-
 template <int D, bool FP8, int RT, int NW, bool QF8, bool PV8>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
 {
@@ -393,44 +387,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a)
             (const uint16_t*)a.q + ((tok0 + (valid ? row[rt] : 0)) * H + head[rt]) * D;
         qsc[rt] = 1.f;
         if constexpr (QF8) {
-            // The vector's largest magnitude (its d-values sit in the four
-            // lanes n + 16 kb), then the smallest 2^e with amax <= 448 2^e
-            // (448 = 0.875 2^9), e >= -117; then q / 2^e (exact) to E4M3,
-            // nearest, ties to even.
-            u32x4 raw[QS][4];
-            float amax = 0.f;
-#pragma unroll
-            for (int st = 0; st < QS; ++st)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    raw[st][j] = valid ? *(const u32x4*)(q + 128 * st + 32 * kb + 8 * j)
-                                       : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[st][j][w])),
-                                                 fabsf(bf16_hi(raw[st][j][w]))));
-                }
-            amax = row_max4(amax);
-            int e = -117;
-            if (amax > 0.f) {
-                int ex;
-                const float mt = frexpf(amax, &ex);
-                e = max(mt <= 0.875f ? ex - 9 : ex - 8, -117);
-            }
-            qsc[rt] = ldexpf(1.f, e);
-#pragma unroll
-            for (int st = 0; st < QS; ++st)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t w0 = raw[st][j][2 * h], w1 = raw[st][j][2 * h + 1];
-                        int c = __builtin_amdgcn_cvt_pk_fp8_f32(
-                            ldexpf(bf16_lo(w0), -e), ldexpf(bf16_hi(w0), -e), 0, false);
-                        c = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(bf16_lo(w1), -e),
-                                                            ldexpf(bf16_hi(w1), -e), c, true);
-                        qf[rt][st][2 * j + h] = c;
-                    }
+            qsc[rt] = qround::round_q<QS>(q, valid, kb, qf[rt]);
         } else {
 #pragma unroll
             for (int st = 0; st < G::KSTEPS; ++st)
@@ -890,6 +847,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream)
         if (!a.fp8)
             return hipErrorNotSupported;
         const int sel = (a.qk_fp8 ? 1 : 0) | (a.pv_fp8 ? 2 : 0);
+        if (sel == 3 && !a.narrow) {
+            // Both bits: the two-role kernel where it serves the shape.
+            const hipError_t e = launch_prefill_pipe(a, stream);
+            if (e != hipErrorNotSupported)
+                return e;
+        }
         if (a.head_dim == 128) {
             switch (sel) {
             case 1: return launch_t<128, true, 1, 8, true, false>(a, stream);
