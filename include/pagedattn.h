@@ -348,7 +348,7 @@ int attn_paged_prefill_fp8(const void* q, int32_t n_rows, const void* k_pool,
  * use, default priority, kept until the process ends), forked from `stream`
  * and joined back to it by events inside the call, so to the caller all of
  * the call's work stays ordered on `stream`; the decode half then takes
- * three quarters of the compute units.  Calls that overlap on one device
+ * seven eighths of the compute units.  Calls that overlap on one device
  * share that second stream and run their chunk halves in turn.  Host
  * checks: n_tok >= 1, 0 <= n_seq_decode <= n_seq, a chunk half needs
  * cu_seqlens, 1 <= max_q_len <= n_tok - n_seq_decode, and a decode-only step

@@ -703,9 +703,9 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
     }
 
     // With both halves, the chunk half runs on a second stream beside the
-    // decode half: the decode kernel (bound by HBM) takes three quarters of
-    // the compute units, and the chunk's workgroups (bound by the matrix
-    // units) start on the rest and fill in beside it.  The chunk then uses
+    // decode half: the decode kernel (bound by HBM) takes seven eighths of
+    // the compute units (one workgroup each), and the chunk's workgroups
+    // (bound by the matrix units) start on the rest and fill in beside it.  The chunk then uses
     // four-wave workgroups, which fit on a CU next to a decode workgroup.
     // Which CU runs a row changes none of its arithmetic.
     const bool both = n_seq_decode > 0 && n_chunk > 0;
@@ -730,7 +730,7 @@ int attn_paged_mixed(const void* q, int32_t n_tok, const int32_t* cu_seqlens, in
         rc = from_hip(side_stream(&side, &cus, &fork, &join), fn);
         if (rc != ATTN_OK)
             return rc;
-        da.max_blocks = da.max_blocks > 0 ? std::min(da.max_blocks, cus * 3 / 4) : cus * 3 / 4;
+        da.max_blocks = da.max_blocks > 0 ? std::min(da.max_blocks, cus * 7 / 8) : cus * 7 / 8;
     }
     if (ev0)
         (void)hipEventRecord(ev0, stream);
