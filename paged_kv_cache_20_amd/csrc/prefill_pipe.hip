@@ -610,6 +610,13 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
             if (i < T) {
                 const int buf = i & 1;
                 const int tile0 = (ts + i) * kKT;
+                // (F8) The scores of tile i + 2 first: their half-length
+                // matrix work then starts before the softmax (measured 2%
+                // faster; slower in the bf16 form, which issues them below).
+                if constexpr (F8) {
+                    scores(kslot(Ph<P + 2>()), sn);
+                    kscales(kcn, (P + 2) % 4);
+                }
                 // Scale (log2 units); on a tile crossing the causal edge or a
                 // row's first key, mask.  Then the lane-local max check.
                 const bool diag = tile0 + kKT - 1 > minpos || tile0 < lo_max;
@@ -708,8 +715,8 @@ __global__ __launch_bounds__(512, 2) void prefill_pipe_kernel(PrefillArgs a)
                 // used), issued beside tile i's probabilities, this lane's part
                 // of the row sums, and the P^T operand: k index j of the 32-key
                 // step is key 16 (j / 4) + 4 kb + j % 4, matching the V^T reads.
-                scores(kslot(Ph<P + 2>()), sn);
-                kscales(kcn, (P + 2) % 4);
+                if constexpr (!F8)
+                    scores(kslot(Ph<P + 2>()), sn);
 #pragma unroll
                 for (int rt = 0; rt < kRT; ++rt) {
                     const float mu = m[rt] == neg_inf() ? 0.f : m[rt];
