@@ -560,7 +560,7 @@ def main():
         print(json.dumps({"calibration": "fill 1 GiB, sum 1 GiB", "sum": float(s)}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: there is no multi-GPU path "
               "(--gpus %d refused)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
