@@ -373,28 +373,43 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
 
     // V B-operands: column n of d-block jb is d = n * DB + jb; k-slot i is
     // the key described at load_tile.
-    uint32_t vb[G::KEYS][G::DB / 2];  // bf16 pairs: dword w = elements 2w, 2w+1
+    // bf16: key pairs (2u, 2u + 1) of one element are gathered from the rows'
+    // bf16 pairs.  fp8: the two keys' code bytes of two elements are gathered
+    // first, then each half widens to that bf16 pair (exact either way).
+    uint32_t vb[FP8 ? 1 : G::KEYS][G::DB / 2];  // bf16 pairs: dword w = elements 2w, 2w+1
+    uint32_t vp8[FP8 ? G::DB : 1][2 * KB];      // fp8: B dword of element jb, key pair u
+    if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < G::KEYS; ++i) {
-        if constexpr (FP8) {
+        for (int u = 0; u < 2 * KB; ++u)
 #pragma unroll
             for (int w = 0; w < G::VDW; ++w) {
-                vb[i][2 * w] = fp8x2_to_bf16x2<false>(t.v[i][w]);
-                vb[i][2 * w + 1] = fp8x2_to_bf16x2<true>(t.v[i][w]);
+                // bytes: key 2u, key 2u + 1 of element 4w, then of 4w + 1 (x);
+                // of 4w + 2 and 4w + 3 (y)
+                const uint32_t x = __builtin_amdgcn_perm(t.v[2 * u + 1][w], t.v[2 * u][w], 0x05010400u);
+                const uint32_t y = __builtin_amdgcn_perm(t.v[2 * u + 1][w], t.v[2 * u][w], 0x07030602u);
+                vp8[4 * w + 0][u] = fp8x2_to_bf16x2<false>(x);
+                vp8[4 * w + 1][u] = fp8x2_to_bf16x2<true>(x);
+                vp8[4 * w + 2][u] = fp8x2_to_bf16x2<false>(y);
+                vp8[4 * w + 3][u] = fp8x2_to_bf16x2<true>(y);
             }
-        } else {
+    } else {
+#pragma unroll
+        for (int i = 0; i < G::KEYS; ++i)
 #pragma unroll
             for (int w = 0; w < G::VDW; ++w)
                 vb[i][w] = t.v[i][w];
-        }
     }
 #pragma unroll
     for (int jb = 0; jb < G::DB; ++jb) {
         const uint32_t sel = (jb & 1) ? 0x07060302u : 0x05040100u;
         uint32_t b[2 * KB];
 #pragma unroll
-        for (int u = 0; u < 2 * KB; ++u)
-            b[u] = __builtin_amdgcn_perm(vb[2 * u + 1][jb >> 1], vb[2 * u][jb >> 1], sel);
+        for (int u = 0; u < 2 * KB; ++u) {
+            if constexpr (FP8)
+                b[u] = vp8[jb][u];
+            else
+                b[u] = __builtin_amdgcn_perm(vb[2 * u + 1][jb >> 1], vb[2 * u][jb >> 1], sel);
+        }
 #pragma unroll
         for (int tau = 0; tau < NT; ++tau) {
             if constexpr (KB == 2) {
