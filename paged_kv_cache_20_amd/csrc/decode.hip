@@ -88,9 +88,10 @@ __device__ __forceinline__ uint32_t bf16_bits(float x)
     return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
 
+// Two floats to a bf16 pair (round to nearest even), one conversion.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
-    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Two e4m3 codes (bytes 2*hi, 2*hi+1 of w) -> two bf16, exact.
