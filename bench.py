@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk, dense
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak
 METRIC = "paged-attn decode µs/step & HBM GB/s (% peak) at 256 seqs; prefill MFMA TFLOP/s"
 
 
@@ -469,6 +470,9 @@ class Bench:
             ms = best[bits]
             res[tag] = {"kernel_median_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                         "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+        # With both bits every product runs on the fp8 matrix unit.
+        res["qk_pv_fp8"]["frac_of_fp8_peak"] = round(
+            fl / (best[qkpv] * 1e-3) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)
         res["flops_per_launch"] = fl
         res["speedup"] = round(best[0] / best[pa.ATTN_PREFILL_FP8_QK], 3)
         res["speedup_qk_pv"] = round(best[0] / best[qkpv], 3)
