@@ -29,6 +29,9 @@
 //   as zeros without touching memory.  No load sits under a branch, so the
 //   compiler's counter waits release each tile as soon as its own loads are
 //   done.  Page ids and fp8 scales are wave-uniform (scalar registers).
+//   bf16 at head_dim 256 with two slot tiles per item streams through two
+//   LDS slots per wave instead (loads that write LDS, two tiles ahead; see
+//   the LR form below).
 //
 // Inside an item (one 64-lane wave)
 //   Query rows are packed into 16-slot MFMA tiles.  A tile holds floor(16/g)
@@ -506,19 +509,73 @@ __device__ __forceinline__ int fetch_pages(const SplitArgs& a, const Item& it, b
     return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)lane * 4u, 0, 0);
 }
 
-template <int D, bool FP8, int NT, bool WIN, bool SSC>
+// LDS tile ring (LR): the form of the split kernel for bf16 at head_dim 256
+// with two slot tiles per item (verify rounds).  Each wave keeps its tile
+// stream in two 16-KiB LDS slots filled by buffer loads that write LDS
+// directly, two tiles ahead of the compute; a tile is copied into registers
+// just before it is computed, and its slot is refilled at once.  A register
+// ring of two-slot-tile items would not fit beside their query operands and
+// accumulators (one tile in flight instead of two), and one slot tile per
+// item would stream every key twice (two sibling items), which halves the
+// distinct bytes in flight.  The arithmetic is the register form's.
+// Batches of at most kMaxSeqLR sequences: the work list shares the LDS.
+constexpr int kMaxSeqLR = 512;
+
+#define LDS __attribute__((address_space(3)))
+
+// The two slots of a wave's LDS ring (TB bytes each), separate LDS arrays so
+// that the compiler can tell a load into one slot from a read of the other.
+template <int TB, int SLOT>
+__device__ __forceinline__ LDS char* lds_slot(int wave)
+{
+    __shared__ __attribute__((aligned(1024))) char ring[kWaves * TB];
+    return (LDS char*)ring + wave * TB;
+}
+
+// A 16-byte-per-lane buffer load that writes LDS directly: lane i's bytes
+// land at dst + 16 i (1 KiB per load); lanes past the resource write zeros.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, LDS char* dst, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)dst, 16, off, 0, 0, 0);
+}
+
+// Waits on this wave's counters, with the compiler kept from moving memory
+// accesses across (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8).  vm_wait<N>: all but the N newest vector-memory
+// accesses have completed (they complete in issue order).  lds_wait: every
+// LDS access has completed.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __asm__ volatile("" ::: "memory");
+}
+__device__ __forceinline__ void lds_wait()
+{
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    __asm__ volatile("" ::: "memory");
+}
+
+template <int D, bool FP8, int NT, bool WIN, bool SSC, bool LR>
 __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(SplitArgs a)
 {
     static_assert(!SSC || FP8, "scalar-unit scales: fp8 only");
+    static_assert(!LR || (D == 256 && !FP8 && NT == 2),
+                  "LDS ring: bf16, head_dim 256, two slot tiles");
     using G = Geo<D, FP8>;
-    constexpr int NBUF = Plan<D, FP8, NT>::NBUF;
+    // Ring period (items are padded to a multiple of it) and depth.
+    constexpr int NBUF = LR ? 2 : Plan<D, FP8, NT>::NBUF;
     constexpr bool PREQ = Plan<D, FP8, NT>::PREQ;
     constexpr int KT = G::KT;
     static_assert(G::CHUNK / 16 <= 64, "one lane per partial-split length class");
-    __shared__ int s_pre[kMaxSeq + 1];  // full items before each sequence
-    __shared__ int s_ord[kMaxSeq];      // sequences with a partial split, longest first
-    __shared__ int s_len[kMaxSeq];
-    __shared__ int s_lo[kMaxSeq];  // first key the sequence's first row attends, -1: none
+    constexpr int MS = LR ? kMaxSeqLR : kMaxSeq;
+    __shared__ int s_pre[MS + 1];  // full items before each sequence
+    __shared__ int s_ord[MS];      // sequences with a partial split, longest first
+    __shared__ int s_len[MS];
+    __shared__ int s_lo[MS];  // first key the sequence's first row attends, -1: none
     // [0, 64): sequences per length class; [64, 128): placed so far; [128,
     // 192): sequences of longer classes; [192, 196): per-wave item sums.
     // Class c (1 .. CHUNK/16) is entry c - 1.
@@ -777,11 +834,67 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
     float ksc, vsc;
     load_q(qop, cur, true);
     load_scales(ksc, vsc, cur, pid, true);
-    Raw<D, FP8> buf[NBUF];
+    // (LR) A tile's 16 loads, each 1 KiB of the slot (lane i's 16 bytes at
+    // 16 i): the K pieces, then the V row pieces, in load_tile's order; read
+    // back by the same lanes into the same registers.
+    using LDSP = LDS char*;
+    constexpr int NLD = G::KLD + 4 * (G::VDW / 4);
+    constexpr int TB = NLD * 1024;
+    LDSP r0 = nullptr;
+    LDSP r1 = nullptr;
+    if constexpr (LR) {
+        r0 = lds_slot<TB, 0>(__builtin_amdgcn_readfirstlane(wave));
+        r1 = lds_slot<TB, 1>(__builtin_amdgcn_readfirstlane(wave));
+    }
+    auto issue_l = [&](LDSP slot, const Item& I, int pidv, bool live, int tile) {
+        if constexpr (LR) {
+            int64_t c0;
+            int n0;
+            page(I, pidv, live, tile, c0, n0);
+            const uint32_t nb = (uint32_t)(n0 * G::ROWB);
+            const __amdgpu_buffer_rsrc_t rk = rsrc(kp + c0 * G::CHUNKB, nb);
+            const __amdgpu_buffer_rsrc_t rv = rsrc(vp + c0 * G::CHUNKB, nb);
 #pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k) {
-        issue(buf[k], cur, pid, true, k);
-        issue_sc(k, cur, pid, true, k);
+            for (int c = 0; c < G::KLD; ++c)
+                load_lds16(rk, slot + 1024 * c, koff + 64 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < G::VDW / 4; ++c)
+                    load_lds16(rv, slot + 1024 * (G::KLD + (G::VDW / 4) * i + c),
+                               voff + i * G::ROWB + 16 * c);
+        }
+    };
+    auto read_l = [&](Raw<D, FP8>& t, LDSP slot) {
+        if constexpr (LR) {
+            typedef LDS u32x4* LQ;
+#pragma unroll
+            for (int c = 0; c < G::KLD; ++c)
+                t.k[0][c] = *(LQ)(slot + 1024 * c + 16 * lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < G::VDW / 4; ++c) {
+                    const int j = G::KLD + (G::VDW / 4) * i + c;
+                    const u32x4 w = *(LQ)(slot + 1024 * j + 16 * lane);
+                    t.v[i][4 * c + 0] = w[0];
+                    t.v[i][4 * c + 1] = w[1];
+                    t.v[i][4 * c + 2] = w[2];
+                    t.v[i][4 * c + 3] = w[3];
+                }
+        }
+    };
+
+    Raw<D, FP8> buf[LR ? 1 : NBUF];
+    if constexpr (LR) {
+        issue_l(r0, cur, pid, true, 0);
+        issue_l(r1, cur, pid, true, 1);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NBUF - 1; ++k) {
+            issue(buf[k], cur, pid, true, k);
+            issue_sc(k, cur, pid, true, k);
+        }
     }
 
     for (;;) {
@@ -842,10 +955,20 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
 #pragma unroll
             for (int k = 0; k < NBUF; ++k) {
                 const int tile = it + k;
-                issue(buf[(k + NBUF - 1) % NBUF], cur, pid, true, tile + NBUF - 1);
-                if (!bad && tile < nt)
-                    compute(buf[k], tile, k);
-                issue_sc((k + NBUF - 1) % NBUF, cur, pid, true, tile + NBUF - 1);
+                if constexpr (LR) {
+                    // Tile `tile` is in slot k, tile + 1 in the other slot.
+                    vm_wait<NLD>();
+                    read_l(buf[0], k ? r1 : r0);
+                    lds_wait();
+                    issue_l(k ? r1 : r0, cur, pid, true, tile + 2);
+                    if (!bad && tile < nt)
+                        compute(buf[0], tile, k);
+                } else {
+                    issue(buf[(k + NBUF - 1) % NBUF], cur, pid, true, tile + NBUF - 1);
+                    if (!bad && tile < nt)
+                        compute(buf[k], tile, k);
+                    issue_sc((k + NBUF - 1) % NBUF, cur, pid, true, tile + NBUF - 1);
+                }
             }
         }
         // The item's last NBUF tiles; the ring moves on to the next item,
@@ -858,16 +981,25 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
 #pragma unroll
         for (int k = 0; k < NBUF; ++k) {
             const int tile = ntp - NBUF + k;
-            if (k == 0)
-                issue(buf[NBUF - 1], cur, pid, true, ntp - 1);
-            else
-                issue(buf[k - 1], nxt, pid_n, has_next, k - 1);
-            if (!bad && tile < nt)
-                compute(buf[k], tile, k);
-            if (k == 0)
-                issue_sc(NBUF - 1, cur, pid, true, ntp - 1);
-            else
-                issue_sc(k - 1, nxt, pid_n, has_next, k - 1);
+            if constexpr (LR) {
+                vm_wait<NLD>();
+                read_l(buf[0], k ? r1 : r0);
+                lds_wait();
+                issue_l(k ? r1 : r0, nxt, pid_n, has_next, k);
+                if (!bad && tile < nt)
+                    compute(buf[0], tile, k);
+            } else {
+                if (k == 0)
+                    issue(buf[NBUF - 1], cur, pid, true, ntp - 1);
+                else
+                    issue(buf[k - 1], nxt, pid_n, has_next, k - 1);
+                if (!bad && tile < nt)
+                    compute(buf[k], tile, k);
+                if (k == 0)
+                    issue_sc(NBUF - 1, cur, pid, true, ntp - 1);
+                else
+                    issue_sc(k - 1, nxt, pid_n, has_next, k - 1);
+            }
         }
 
         // Partials: O rows are slots 4*kb + r; m, l of slot n.  Bounds-checked
@@ -925,6 +1057,10 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         ksc = ksc_n;
         vsc = vsc_n;
     }
+    // (LR) The last tiles' loads (of no item: they write zeros) land before
+    // the wave ends and its LDS can be given to another workgroup.
+    if constexpr (LR)
+        __builtin_amdgcn_s_waitcnt(0);
 }
 
 // One wave per (sequence, row, head); lanes own D/64 consecutive d-values.
@@ -1026,7 +1162,7 @@ __global__ __launch_bounds__(256) void combine_kernel(SplitArgs a)
         out[e] = nan ? (uint16_t)0x7FC0 : (uint16_t)bf16_bits(num[e] / den);
 }
 
-template <int D, bool FP8, int NT, bool WIN>
+template <int D, bool FP8, int NT, bool WIN, bool LR = false>
 hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
 {
     using G = Geo<D, FP8>;
@@ -1044,8 +1180,12 @@ hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess)
             return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, split_kernel<D, FP8, NT, WIN, false>,
-                                                         256, 0);
+        if constexpr (LR)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per, split_kernel<D, FP8, NT, WIN, false, true>, 256, 0);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per, split_kernel<D, FP8, NT, WIN, false, false>, 256, 0);
         if (e != hipSuccess)
             return e;
         // 1024-key splits: one workgroup per CU keeps about as many items per
@@ -1071,16 +1211,19 @@ hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
     if (a.phase != 2) {
         if (a.ev_start)
             (void)hipEventRecord(a.ev_start, stream);
-        if constexpr (CAN_SSC) {
+        if constexpr (LR) {
+            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, true>),
+                               dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        } else if constexpr (CAN_SSC) {
             if (ssc)
-                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, true>), dim3((unsigned)blocks),
-                                   dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, true, false>),
+                                   dim3((unsigned)blocks), dim3(256), 0, stream, a);
             else
-                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false>), dim3((unsigned)blocks),
-                                   dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, false>),
+                                   dim3((unsigned)blocks), dim3(256), 0, stream, a);
         } else {
-            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false>), dim3((unsigned)blocks),
-                               dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, false>),
+                               dim3((unsigned)blocks), dim3(256), 0, stream, a);
         }
         e = hipGetLastError();
         if (e != hipSuccess)
@@ -1102,7 +1245,10 @@ hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
 // in any tile of any instantiation, so this changes no bit of the output.
 // Measured: at head_dim 128 two tiles per item beat one (fp8, 8 rows x 4
 // heads) and four (bf16, 8 rows x 8 heads: 514 -> 299 us); at head_dim 256
-// one tile per item equals two.
+// with the register ring one tile per item equals two (two tiles leave
+// room for one tile in flight).  bf16 at head_dim 256 with two or more
+// tiles takes the LDS-ring form with two tiles per item where the batch
+// fits its work list.
 template <int D>
 int kernel_tiles(int nt)
 {
@@ -1112,8 +1258,14 @@ int kernel_tiles(int nt)
 template <int D, bool FP8, bool WIN>
 hipError_t launch_nt_w(const SplitArgs& a0, int nt, hipStream_t stream)
 {
-    const int ntk = kernel_tiles<D>(nt);
     SplitArgs a = a0;
+    if constexpr (D == 256 && !FP8) {
+        if (nt >= 2 && a.n_seq <= kMaxSeqLR) {
+            a.slices = nt / 2;
+            return launch_split_t<D, FP8, 2, WIN, true>(a, stream);
+        }
+    }
+    const int ntk = kernel_tiles<D>(nt);
     a.slices = nt / ntk;
     switch (ntk) {
     case 1: return launch_split_t<D, FP8, 1, WIN>(a, stream);
