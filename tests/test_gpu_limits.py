@@ -52,6 +52,32 @@ def test_largest_batch(rows, fp8):
     torch.cuda.empty_cache()
 
 
+def test_verify_d256_either_side_of_the_lds_ring_batch():
+    """bf16 verify rounds at head_dim 256 run the split kernel's LDS-ring
+    form for batches of at most 512 sequences and the register form (one
+    slot tile per item) above: the same rows give the same bits either way."""
+    n = 600
+    lens = short_lengths(n, 8, 171)
+    w = synth.listed("ring_edge_d256", lens, 8, 16, 4, 256, False, 172, kind="verify")
+    say("[gpu] verify d256 batch", n)
+    inp = synth.draw(w, "cuda")
+    gpu = GpuCache(inp)
+    out = gpu.run("verify")  # register form
+    torch.cuda.synchronize()
+    seqs = [0, 3, 299, 597, n - 1]
+    oc = OracleCache(inp, seqs)
+    ref = oc.attend(inp.q)
+    assert excess_err(out.index_select(0, torch.tensor(seqs, device="cuda")), ref, TOL[False]) <= 0
+    for part in (torch.arange(0, 512, device="cuda"), torch.arange(88, n, device="cuda")):
+        out2 = gpu.run("verify", q=inp.q.index_select(0, part).contiguous(),
+                       lengths=inp.lengths.index_select(0, part).contiguous(),
+                       table=inp.table.index_select(0, part).contiguous())  # LDS-ring form
+        torch.cuda.synchronize()
+        assert same_bits(out2, out.index_select(0, part))
+    del gpu, inp
+    torch.cuda.empty_cache()
+
+
 def test_batch_above_the_limit_is_refused():
     lens = [4] * (MAX_SEQ + 1)
     w = synth.listed("too_many", lens, 1, 8, 2, 128, False, 150)
