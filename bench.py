@@ -22,6 +22,13 @@ rounds and the mixed decode + chunk step.  `cpu_baseline` is the CPU oracle
 timed over the whole headline workload on this host (repeated to about 10 s,
 median pass).
 
+Every timed line first repeats its call untimed: at least W calls and at
+least WARM_S seconds of them.  The GPU's clocks rise over the first tens of
+milliseconds of load after an idle spell (measured per launch: the prefill
+chunk takes 2.6 ms at a cold start and settles at 1.83 ms after about 40 ms
+of launches; after 2 s idle it starts again at 2.2 ms), so a line timed
+within that ramp would report the ramp, not the kernel.
+
 `roofline.traffic` is the measured HBM bytes per launch of the timed kernel,
 read from profiles/hbm_traffic.json when that file was taken on the current
 kernel sources (else null).  It comes from rocprofv3 FETCH_SIZE and
@@ -47,6 +54,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak
 METRIC = "paged-attn decode µs/step & HBM GB/s (% peak) at 256 seqs; prefill MFMA TFLOP/s"
+WARM_S = 0.25  # least untimed run time of a call before it is timed (seconds)
 
 
 def log(*a):
@@ -144,6 +152,18 @@ class Bench:
         self.torch, self.pa, self.synth = torch, pa, synth
         self.ev = HipEvents()
 
+    def warm(self, fn, n):
+        """Untimed calls of fn: at least n, and at least WARM_S seconds of
+        them (the device drained every 8 calls, so the time is the GPU's)."""
+        t0 = time.perf_counter()
+        i = 0
+        while i < n or time.perf_counter() - t0 < WARM_S:
+            fn()
+            i += 1
+            if i % 8 == 0:
+                self.torch.cuda.synchronize()
+        self.torch.cuda.synchronize()
+
     def setup_split(self, name, spare_pages=0):
         torch, pa, synth = self.torch, self.pa, self.synth
         w = synth.WORKLOADS[name]
@@ -197,9 +217,7 @@ class Bench:
 
     def time_split(self, st, steps, warmup):
         torch = self.torch
-        for _ in range(warmup):
-            self.split_step(st)
-        torch.cuda.synchronize()
+        self.warm(lambda: self.split_step(st), warmup)
         evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
         marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
@@ -280,9 +298,7 @@ class Bench:
         res = {}
         for tag, fn in (("mixed_call", mixed), ("decode_half", dec_half),
                         ("chunk_half", chunk_half)):
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
+            self.warm(fn, warmup)
             # The library launches on torch's current stream, so torch's
             # events bracket each whole call (all of its kernels).
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -317,9 +333,7 @@ class Bench:
                                         inp.n_pages, inp.table, w.max_pages, inp.lengths,
                                         w.n_seq, window, None, w.n_head, w.n_head_kv,
                                         w.head_dim, 16, st["kv"], st["out"], st["ws"], st["wsb"])
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
+        self.warm(call, warmup)
         evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
         for i in range(steps):
             pa.attn_set_kernel_timer(evs[i][0], evs[i][1])
@@ -361,9 +375,7 @@ class Bench:
                                            inp.table, w.max_pages, inp.lengths, w.n_seq, width,
                                            w.n_head, w.n_head_kv, w.head_dim, 16, st["kv"], out,
                                            st["ws"], st["wsb"])
-            for _ in range(warmup):
-                call()
-            torch.cuda.synchronize()
+            self.warm(call, warmup)
             evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
             for i in range(steps):
                 pa.attn_set_kernel_timer(evs[i][0], evs[i][1])
@@ -405,9 +417,7 @@ class Bench:
                                       inp.table, w.max_pages, inp.lengths, S, width, mask_d,
                                       scratch, w.n_head, w.n_head_kv, w.head_dim, 16, st["kv"],
                                       out, ws, wsb)
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
+        self.warm(call, warmup)
         kev = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
@@ -450,9 +460,7 @@ class Bench:
                                               st["vs"], inp.n_pages, inp.table, w.max_pages,
                                               st["C"], w.n_head, w.n_head_kv, w.head_dim, 16,
                                               st["kv"], bits, st["out"])
-                for _ in range(warmup):
-                    call()
-                torch.cuda.synchronize()
+                self.warm(call, warmup)
                 evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
                 for i in range(steps):
                     call(evs[i])
@@ -482,9 +490,7 @@ class Bench:
 
     def time_prefill(self, st, steps, warmup):
         torch = self.torch
-        for _ in range(warmup):
-            self.prefill_step(st)
-        torch.cuda.synchronize()
+        self.warm(lambda: self.prefill_step(st), warmup)
         evs = [(self.ev.create(), self.ev.create()) for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
