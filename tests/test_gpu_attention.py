@@ -101,6 +101,33 @@ def test_verify_rows_equal_decode_rows_bitwise(small):
         assert same_bits(dec[:, 0], out[:, r]), "row %d" % r
 
 
+@pytest.mark.parametrize("g", [4, 8])
+def test_head_dim_256_rounds_equal_decode_rows_random_lengths(g):
+    """bf16 rounds at head_dim 256 (the split kernel's LDS-ring form: both
+    slot tiles of a (sequence, split, kv head) in one item) over lengths that
+    put the round on split, tile and page boundaries and near the start:
+    every row is bit for bit the decode row at its position, and the rows
+    meet the oracle."""
+    rng = np.random.default_rng(600 + g)
+    lens = [8, 9, 15, 16, 17, 23, 24, 31, 511, 512, 513, 519, 520, 1023, 1031, 1536, 1543]
+    lens += [int(c) for c in rng.integers(8, 2600, size=23)]
+    w = synth.listed("ring_rand_g%d" % g, lens, 8, 4 * g, 4, 256, False, 610 + g, kind="verify")
+    say("[gpu] head_dim 256 rounds, g", g, "lengths", lens)
+    inp = synth.draw(w, "cuda")
+    gpu = GpuCache(inp)
+    out = gpu.run("verify")
+    torch.cuda.synchronize()
+    for r in range(8):
+        dec = gpu.run("decode", q=inp.q[:, r:r + 1].contiguous(), lengths=inp.lengths - 8 + r + 1)
+        torch.cuda.synchronize()
+        assert same_bits(dec[:, 0], out[:, r]), "row %d" % r
+    seqs = [0, 4, 8, 11, 16, 30]
+    ref = OracleCache(inp, seqs).attend(inp.q)
+    assert excess_err(out.index_select(0, torch.tensor(seqs, device="cuda")), ref, TOL[False]) <= 0
+    del gpu, inp
+    torch.cuda.empty_cache()
+
+
 def test_batch_invariance(small):
     """Each sequence alone, and the batch reversed, give the same bits."""
     w, inp, gpu, out = small
