@@ -281,7 +281,7 @@ __device__ __forceinline__ int slot_row(int slot, int tau, int g, int ppt, int R
     return r < R ? r : -1;
 }
 
-template <int D, bool FP8, int NT, bool WIN>
+template <int D, bool FP8, int NT, bool WIN, bool ILP>
 __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (&qop)[NT][D / 32],
                                              const int (&first)[NT], const int (&last)[NT],
                                              float (&m)[NT], float (&l)[NT],
@@ -359,10 +359,12 @@ __device__ __forceinline__ void compute_tile(const Raw<D, FP8>& t, const u32x4 (
     }
 
     // Rescale O rows (slot 4*kb + r) by their slot's alpha; skipping a
-    // multiply by exactly 1 changes nothing.
+    // multiply by exactly 1 changes nothing (ILP: always multiplied, so
+    // the tile has no branch and the tiles of a ring round share one
+    // scheduling block).
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
-        if (__builtin_amdgcn_ballot_w64(alpha[tau] != 1.f)) {
+        if (ILP || __builtin_amdgcn_ballot_w64(alpha[tau] != 1.f)) {
             float ar[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -559,7 +561,12 @@ __device__ __forceinline__ void lds_wait()
     __asm__ volatile("" ::: "memory");
 }
 
-template <int D, bool FP8, int NT, bool WIN, bool SSC, bool LR>
+// ILP (calls with at most one work item per wave, where a tile's time is
+// the wave's own instruction stream): the tile loop has no branch -- the
+// rescale is always applied, a main-loop tile is never a padding tile and a
+// bad item's tiles (which load nothing) are computed and then discarded --
+// so the compiler interleaves the tiles of a ring round.  Same bits.
+template <int D, bool FP8, int NT, bool WIN, bool SSC, bool LR, bool ILP>
 __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(SplitArgs a)
 {
     static_assert(!SSC || FP8, "scalar-unit scales: fp8 only");
@@ -730,7 +737,12 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
         chunk = (int64_t)(ok ? p : 0) * Hk + I.kh;
         // (readfirstlane keeps the clamp, which only the vector unit has,
         // from turning the buffer resources into per-lane values.)
-        rows = ok ? __builtin_amdgcn_readfirstlane(min(16, max(0, I.t1 - (I.t0 + 16 * e)))) : 0;
+        if constexpr (ILP) {
+            const int rr = __builtin_amdgcn_readfirstlane(min(16, max(0, I.t1 - (I.t0 + 16 * e))));
+            rows = ok ? rr : 0;
+        } else {
+            rows = ok ? __builtin_amdgcn_readfirstlane(min(16, max(0, I.t1 - (I.t0 + 16 * e)))) : 0;
+        }
     };
     auto issue = [&](Raw<D, FP8>& buf, const Item& I, int pidv, bool live, int tile) {
         const int e0 = tile * G::KB;
@@ -938,13 +950,13 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
             const int e1 = G::KB == 2 ? e0 + 1 : e0;
             if constexpr (SSC) {
                 constexpr int L = G::KB - 1;
-                compute_tile<D, FP8, NT, WIN>(
+                compute_tile<D, FP8, NT, WIN, ILP>(
                     t, qop, first, last, m, l, O, t0 + KT * tile,
                     (sr[slot][0] > 0 ? sk[slot][0] : 0.f) * sm_log2,
                     (sr[slot][L] > 0 ? sk[slot][L] : 0.f) * sm_log2,
                     sr[slot][0] > 0 ? sv[slot][0] : 0.f, sr[slot][L] > 0 ? sv[slot][L] : 0.f, kb);
             } else {
-                compute_tile<D, FP8, NT, WIN>(t, qop, first, last, m, l, O, t0 + KT * tile,
+                compute_tile<D, FP8, NT, WIN, ILP>(t, qop, first, last, m, l, O, t0 + KT * tile,
                                               kscale(e0), kscale(e1), vscale(e0), vscale(e1),
                                               kb);
             }
@@ -965,7 +977,7 @@ __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(Spl
                         compute(buf[0], tile, k);
                 } else {
                     issue(buf[(k + NBUF - 1) % NBUF], cur, pid, true, tile + NBUF - 1);
-                    if (!bad && tile < nt)
+                    if (ILP || (!bad && tile < nt))
                         compute(buf[k], tile, k);
                     issue_sc((k + NBUF - 1) % NBUF, cur, pid, true, tile + NBUF - 1);
                 }
@@ -1182,10 +1194,10 @@ hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
             return e;
         if constexpr (LR)
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per, split_kernel<D, FP8, NT, WIN, false, true>, 256, 0);
+                &per, split_kernel<D, FP8, NT, WIN, false, true, false>, 256, 0);
         else
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per, split_kernel<D, FP8, NT, WIN, false, false>, 256, 0);
+                &per, split_kernel<D, FP8, NT, WIN, false, false, false>, 256, 0);
         if (e != hipSuccess)
             return e;
         // 1024-key splits: one workgroup per CU keeps about as many items per
@@ -1208,21 +1220,29 @@ hipError_t launch_split_t(const SplitArgs& a0, hipStream_t stream)
     // forms compute the same bits.
     constexpr bool CAN_SSC = FP8 && Plan<D, FP8, NT>::NBUF == 4;
     const bool ssc = CAN_SSC && (int64_t)a.n_seq * Hk * a.slices >= 2 * blocks * kWaves;
+    // The branch-free tile loop where every wave has at most one item
+    // (decode without a window).  Both forms compute the same bits.
+    constexpr bool CAN_ILP = NT == 1 && !WIN && !LR;
+    const bool ilp = CAN_ILP && upper <= blocks * kWaves;
     if (a.phase != 2) {
         if (a.ev_start)
             (void)hipEventRecord(a.ev_start, stream);
         if constexpr (LR) {
-            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, true>),
+            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, true, false>),
                                dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        } else if (CAN_ILP && ilp) {
+            if constexpr (CAN_ILP)
+                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, false, true>),
+                                   dim3((unsigned)blocks), dim3(256), 0, stream, a);
         } else if constexpr (CAN_SSC) {
             if (ssc)
-                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, true, false>),
+                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, true, false, false>),
                                    dim3((unsigned)blocks), dim3(256), 0, stream, a);
             else
-                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, false>),
+                hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, false, false>),
                                    dim3((unsigned)blocks), dim3(256), 0, stream, a);
         } else {
-            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, false>),
+            hipLaunchKernelGGL((split_kernel<D, FP8, NT, WIN, false, false, false>),
                                dim3((unsigned)blocks), dim3(256), 0, stream, a);
         }
         e = hipGetLastError();
