@@ -563,9 +563,10 @@ __device__ __forceinline__ void lds_wait()
 
 // ILP (calls with at most one work item per wave, where a tile's time is
 // the wave's own instruction stream): the tile loop has no branch -- the
-// rescale is always applied, a main-loop tile is never a padding tile and a
-// bad item's tiles (which load nothing) are computed and then discarded --
-// so the compiler interleaves the tiles of a ring round.  Same bits.
+// rescale is always applied, a main-loop tile is never a padding tile and
+// the tiles of an item with a page outside the pool (such pages load
+// nothing) are computed and their result replaced by NaN as in the other
+// form -- so the compiler interleaves the tiles of a ring round.  Same bits.
 template <int D, bool FP8, int NT, bool WIN, bool SSC, bool LR, bool ILP>
 __global__ __launch_bounds__(256, (Plan<D, FP8, NT>::OCC)) void split_kernel(SplitArgs a)
 {
